@@ -1,0 +1,45 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin (CPU only).
+
+Each mutant is a one-line edit of ``oracle/attention_ref.py`` written to a temporary file; the pin
+suite ``tests/test_oracle.py`` is then run against it in a subprocess and must fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attention_ref.py")
+
+MUTANTS = {
+    "scale dropped": ("return float(scale) * (q @ k.T)", "return (q @ k.T)"),
+    "causal mask off by one": ("<= (rows[:, None] + (Tk - Tq))", "< (rows[:, None] + (Tk - Tq))"),
+    "causal mask top-left aligned": ("(rows[:, None] + (Tk - Tq))", "(rows[:, None] + 0)"),
+    "keys used as values": ("softmax_attend(S, v, vis)", "softmax_attend(S, k[:, :v.shape[1]], vis)"),
+    "log2 instead of ln": ("LSE = m[:, 0] + np.log(ell[:, 0])", "LSE = m[:, 0] + np.log2(ell[:, 0])"),
+    "exponent sign flipped": ("P = np.exp(S - m)", "P = np.exp(-(S - m))"),
+    "not normalised": ("    P /= ell\n", "    pass\n"),
+    "max not subtracted": ("P = np.exp(S - m)", "P = np.exp(S)"),
+    "recurrence output not rescaled": ("o[t] = o[t] * c + sum(", "o[t] = o[t] + sum("),
+    "recurrence denominator not rescaled": ("ell = ell * c + sum(p.values())",
+                                            "ell = ell + sum(p.values())"),
+    "combine weight inverted": ("else math.exp(m - m_star)", "else math.exp(m_star - m)"),
+    "split chunk drops a key": ("min(Tk, (s + 1) * chunk)", "min(Tk, (s + 1) * chunk - 1)"),
+    "lse of split uses wrong max": ("return o / ell, m_star + math.log(ell)",
+                                    "return o / ell, math.log(ell)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    path = tmp_path / "mutant.py"
+    path.write_text(src.replace(old, new))
+    env = dict(os.environ, FA_ORACLE_MUTANT_FILE=str(path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
