@@ -1,0 +1,235 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal attention forward at B=8, h=32, T=4096, d_head=128 (bf16, fp32 accumulate)
+plus one split-KV decode at B=64, h=32, Tk=8192, d_head=128 with 16 splits.  Inputs are seeded
+synthetic N(0,1) bf16 tensors, resident in HBM before timing starts.  W warm-up steps, then K timed
+steps between two device synchronisations; every library call is bracketed by HIP events on the
+stream it is launched on, which gives each kernel's average duration.
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value    = forward TFLOP/s (4*B*h*T*T*d/2 FLOPs / average forward duration)
+  roofline = that kernel against the MI355X dense-bf16 MFMA peak
+  decode   = decode HBM GB/s (K+V bytes / average decode duration) against the HBM peak
+  cpu_baseline = the fp64 CPU oracle timed on a bounded sample of the same forward workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PREFILL = "causal_b8_h32_t4096_d128"
+DECODE = "decode_b64_h32_tk8192_d128_s16"
+METRIC = "attention fwd TFLOP/s (% MFMA peak) at T=4096 causal; decode HBM GB/s (% peak)"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def upload(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary, if any.
+
+    The summary file (profiles/<kernel_tag>_traffic.json) holds FETCH_SIZE / WRITE_SIZE per
+    dispatch already scaled by the copy-kernel calibration factor, and the hash of the kernel
+    source it was taken on; a stale summary (source changed since) gives null.
+    """
+    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        import hashlib
+        src = os.path.join(ROOT, rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return float(rec["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(seconds_budget: float):
+    """Time the fp64 oracle on whole heads of the forward workload (same generator, seed 0)."""
+    import numpy as np
+    import seeded_inputs as si
+    from io_aware_attention_fa_amd import costmodel as cm
+    from oracle import attention_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = si.WORKLOADS[PREFILL]
+    heads, elapsed = 0, 0.0
+    while heads == 0 or (elapsed < seconds_budget and heads < wl.B * wl.h):
+        b, h = divmod(heads, wl.h)
+        q, k, v = si.head_inputs(wl, 0, b, h)
+        q, k, v = si.bf16_bits_to_f64(q), si.bf16_bits_to_f64(k), si.bf16_bits_to_f64(v)
+        t0 = time.perf_counter()
+        ref.naive_attention_head(q, k, v, wl.scale, True)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    flops = cm.attention_flops(1, heads, wl.Tq, wl.Tk, wl.d, True)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} whole heads (4096x4096 causal, d=128) of {PREFILL}, "
+                      f"{elapsed:.1f} s of fp64 numpy; FLOPs counted as 4*T*T*d/2 per head"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one half of the step (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        eprint("bench.py measures one GPU: this build has no multi-GPU path (every GPU box has one "
+               "GPU). Run with --gpus 1.")
+        sys.exit(2)
+
+    import torch
+
+    import io_aware_attention_fa_amd as fa
+    import seeded_inputs as si
+    from io_aware_attention_fa_amd import costmodel as cm
+
+    if not torch.cuda.is_available():
+        eprint("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+    eprint(f"[bench] device {props.name} CUs={props.multi_processor_count} lib={fa.LIB_PATH}")
+
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
+    wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
+
+    t0 = time.perf_counter()
+    if do_prefill:
+        q, k, v = si.make_inputs(wp, seed=0)
+        pq, pk, pv = upload(q), upload(k), upload(v)
+        po = torch.empty_like(pq)
+        plse = torch.empty((wp.B, wp.h, wp.Tq), dtype=torch.float32, device="cuda")
+        del q, k, v
+    if do_decode:
+        q, k, v = si.make_inputs(wd, seed=0)
+        dq, dk, dv = upload(q), upload(k), upload(v)
+        do = torch.empty_like(dq)
+        dlse = torch.empty((wd.B, wd.h), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_decode_workspace_size(wd.B, wd.h, wd.d, wd.num_splits),
+                         dtype=torch.uint8, device="cuda")
+        del q, k, v
+    torch.cuda.synchronize()
+    eprint(f"[bench] inputs generated and resident in {time.perf_counter() - t0:.1f} s")
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2**20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        eprint(f"[bench] copy probe of {n} bytes done")
+
+    def step(evs=None, i=0):
+        if do_prefill:
+            if evs:
+                evs["p0"][i].record()
+            fa.fa_fwd(pq, pk, pv, causal=True, scale=wp.scale, o=po, lse=plse)
+            if evs:
+                evs["p1"][i].record()
+        if do_decode:
+            if evs:
+                evs["d0"][i].record()
+            fa.fa_decode(dq, dk, dv, num_splits=wd.num_splits, scale=wd.scale, o=do, lse=dlse,
+                         workspace=ws)
+            if evs:
+                evs["d1"][i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = {key: [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+           for key in ("p0", "p1", "d0", "d1")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eprint(f"[bench] {K} steps in {wall * 1e3:.1f} ms")
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    config = {"workload": f"{PREFILL} + {DECODE}" if args.only is None else
+              (PREFILL if do_prefill else DECODE)}
+
+    if do_prefill:
+        pt = [evs["p0"][i].elapsed_time(evs["p1"][i]) for i in range(K)]
+        p_ms = sum(pt) / K
+        flops = cm.attention_flops(wp.B, wp.h, wp.Tq, wp.Tk, wp.d, True)
+        tflops = flops / (p_ms * 1e-3) / 1e12
+        peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
+        out.update(value=tflops, unit="TFLOP/s")
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                           "frac": tflops / peak,
+                           "traffic": traffic_from_profiles("fa_fwd_kernel_d128_causal")}
+        config.update(prefill={"B": wp.B, "h": wp.h, "T": wp.Tq, "d_head": wp.d, "causal": True,
+                               "avg_ms": p_ms, "min_ms": min(pt), "median_ms": sorted(pt)[K // 2],
+                               "alg_bytes": cm.attention_io_bytes(wp.B, wp.h, wp.Tq, wp.Tk, wp.d),
+                               "flops": flops})
+        eprint(f"[bench] prefill avg {p_ms:.4f} ms  {tflops:.1f} TFLOP/s  "
+               f"{100 * tflops / peak:.1f}% of {peak:.0f}")
+    if do_decode:
+        dt = [evs["d0"][i].elapsed_time(evs["d1"][i]) for i in range(K)]
+        d_ms = sum(dt) / K
+        kv = wd.B * wd.h * wd.Tk * cm.decode_kv_bytes_per_token(wd.d)
+        gbs = kv / (d_ms * 1e-3) / 1e9
+        peak_gbs = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
+        dec = {"metric": "decode HBM GB/s (K+V bytes / split+combine time)", "value": gbs,
+               "unit": "GB/s",
+               "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak_gbs, "unit": "GB/s",
+                            "frac": gbs / peak_gbs,
+                            "traffic": traffic_from_profiles("fa_decode_split_kernel_d128")},
+               "avg_ms": d_ms, "min_ms": min(dt), "median_ms": sorted(dt)[K // 2],
+               "config": {"B": wd.B, "h": wd.h, "Tk": wd.Tk, "d_head": wd.d,
+                          "num_splits": wd.num_splits}}
+        out["decode"] = dec
+        eprint(f"[bench] decode avg {d_ms:.4f} ms  {gbs:.0f} GB/s  {100 * gbs / peak_gbs:.1f}%")
+        if not do_prefill:
+            out.update(value=gbs, unit="GB/s", roofline=dec["roofline"])
+    out["config"] = config
+
+    if do_prefill and not args.no_cpu_baseline:
+        eprint("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) IO-aware attention library (libfa_mi355x.so).
+ *
+ * What it computes.  For every batch b and head h, with S = scale * Q K^T:
+ *     O   = softmax(S masked) V                  (row softmax over the visible keys)
+ *     LSE = log(sum_j exp(S_ij)) over visible j   (natural log, one fp32 per query row)
+ * This is the forward pass of FlashAttention-style attention as defined on the page
+ * "Kernels -- fusion and FlashAttention" (section 3, the online-softmax recurrence, and section 5,
+ * the Triton tile program that writes O and m + log l), computed without ever storing the
+ * Tq x Tk score matrix: query rows are tiled into blocks, K/V tiles stream through on-chip
+ * memory, and a running max m, denominator l and output accumulator o are kept per query row
+ * (page "Fusion and IO-aware kernels", "How it really works", FlashAttention steps 1-4).
+ * The result is exact softmax attention up to floating-point rounding.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers (memory from hipMalloc / torch on the GPU), row-major
+ *     and contiguous.  bf16 tensors are passed as raw 16-bit bfloat16 storage.
+ *   - Ownership: the caller allocates and frees every buffer (outputs and the decode workspace).
+ *     The library never allocates, frees, memsets or synchronises; it writes every element of
+ *     every output it is given.
+ *   - Asynchrony: a successful call only enqueues work on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream) and returns FA_OK.  Results are valid once the caller has
+ *     synchronised that stream.
+ *   - Errors: arguments are validated on the host before any HIP call.  An invalid call returns a
+ *     nonzero FA_ERR_* code, enqueues nothing and leaves every output untouched.  A failed kernel
+ *     launch returns FA_ERR_HIP; fa_last_hip_error() then gives the hipError_t (per thread).
+ *     No C++ exception crosses this interface.
+ *   - Thread safety: the library holds no state besides the per-thread last HIP error.
+ *   - Precision: bf16 inputs, fp32 accumulation of both contractions and of the softmax state,
+ *     P rounded to bf16 (round to nearest even) before the P V contraction, O rounded to bf16
+ *     (round to nearest even) at the end, LSE in fp32.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,             /* a required pointer is NULL                                    */
+  FA_ERR_SHAPE = 2,            /* a size is < 1, or too large for the kernels' 32-bit offsets   */
+  FA_ERR_HEAD_DIM = 3,         /* d_head is not 64 or 128                                       */
+  FA_ERR_CAUSAL_TQ_GT_TK = 4,  /* causal with Tq > Tk (a query row would see no key)            */
+  FA_ERR_ALIGN = 5,            /* a tensor pointer is not 16-byte aligned (LSE: 4-byte)          */
+  FA_ERR_SCALE = 6,            /* scale is not finite, or causal is not 0 / 1                   */
+  FA_ERR_SPLITS = 7,           /* num_splits outside [1, min(Tk, FA_MAX_SPLITS)]                */
+  FA_ERR_WORKSPACE = 8,        /* decode workspace NULL, misaligned or smaller than required     */
+  FA_ERR_HIP = 9               /* a HIP launch failed; see fa_last_hip_error()                  */
+};
+
+/* Largest per-head tensor the kernels address with 32-bit byte offsets: T * d_head * 2 bytes
+ * must stay below 2^31 (so T <= 8,388,607 at d_head = 128). */
+#define FA_MAX_HEAD_BYTES 2147483647LL
+/* Largest split count of the decode entry point. */
+#define FA_MAX_SPLITS 256
+
+/*
+ * fa_fwd -- attention forward (prefill).
+ *   q    [B][h][Tq][d_head] bf16        k, v [B][h][Tk][d_head] bf16
+ *   o    [B][h][Tq][d_head] bf16 (out)  lse  [B][h][Tq] fp32 (out, natural log)
+ *   causal = 1: query i sees key j iff j <= i + (Tk - Tq) (bottom-right aligned; with Tq == Tk
+ *     the lower triangle including the diagonal).  Key tiles entirely above the diagonal are
+ *     skipped and the diagonal tiles are masked on chip (page "Chapter 10 Writing and Benchmarking
+ *     Custom Kernels", section 10.3.1, "What You Actually Decide in Practice": causal masking and
+ *     the final partial tile).  causal = 0: every key is visible.
+ *   scale multiplies Q K^T before the softmax (usually 1/sqrt(d_head)); it must be finite.
+ *   Preconditions: B, h, Tq, Tk >= 1; d_head in {64, 128}; causal => Tq <= Tk;
+ *   q, k, v, o 16-byte aligned, lse 4-byte aligned; Tq*d_head*2 and Tk*d_head*2 <= FA_MAX_HEAD_BYTES.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+           int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_o32 -- the same computation and kernel, with O stored in fp32 instead of bf16.
+ *   o [B][h][Tq][d_head] fp32 (out).  For parity diagnostics: the bf16 output of fa_fwd is the
+ *   round-to-nearest-even of this output, bit for bit.  Same preconditions as fa_fwd.
+ */
+int fa_fwd_o32(const void* q, const void* k, const void* v, float* o, float* lse,
+               int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+               int causal, float scale, void* stream);
+
+/*
+ * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
+ *   B * h * num_splits * (d_head + 2) fp32 partials (chunk max, denominator, d_head outputs).
+ *   Returns 0 for sizes < 1.
+ */
+size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t num_splits);
+
+/*
+ * fa_decode -- split-KV decode: one query per (batch, head) against a KV cache, no mask.
+ *   q [B][h][d_head] bf16; k, v [B][h][Tk][d_head] bf16; o [B][h][d_head] bf16 (out);
+ *   lse [B][h] fp32 (out).  The Tk keys are cut into num_splits chunks of ceil(Tk/num_splits)
+ *   keys; one pass computes each chunk's (max, denominator, unnormalised output) into
+ *   `workspace`, a second pass rescales the chunks onto their common max and normalises
+ *   (page "Fusion and IO-aware kernels", "Where it breaks": decode is KV-cache bound and is split
+ *   across the sequence; the merge is the rescale of the online-softmax recurrence).
+ *   The result does not depend on num_splits beyond rounding.
+ *   Preconditions: as fa_fwd for pointers and sizes; 1 <= num_splits <= min(Tk, FA_MAX_SPLITS);
+ *   workspace 16-byte aligned with workspace_bytes >= fa_decode_workspace_size(B, h, d_head,
+ *   num_splits).  The workspace holds no state between calls.
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
+              int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32 and fa_decode (no HIP call is made).
+ * Return FA_OK or the FA_ERR_* code the entry point would return. */
+int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                    int causal, float scale);
+int fa_validate_decode(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int64_t B, int64_t h, int64_t Tk, int64_t d_head,
+                       float scale, int64_t num_splits, const void* workspace,
+                       size_t workspace_bytes);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* The hipError_t behind this thread's last FA_ERR_HIP (0 if none). */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,1 +1,157 @@
-"""MI355X-native IO-aware attention forward and split-KV decode (placeholder until the binding)."""
+"""MI355X-native IO-aware attention: fused attention forward and split-KV decode.
+
+A thin binding over the C ABI of ``include/fa.h`` (``libfa_mi355x.so``).  The functions carry the
+same names as the C entry points and only marshal arguments: torch supplies device memory and the
+current stream, every step of the computation runs in the library's HIP kernels.  There is no CPU
+fallback; importing this package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR_HIP,  # noqa: F401
+                   FA_ERR_NULL, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS, FA_ERR_WORKSPACE,
+                   FA_OK, LIB_PATH)
+
+__all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_validate_fwd",
+           "fa_validate_decode", "fa_status_str", "fa_last_hip_error", "FaError", "LIB_PATH"]
+
+
+class FaError(RuntimeError):
+    """A nonzero status returned by the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        msg = fa_status_str(status)
+        if status == FA_ERR_HIP:
+            msg += f" (hipError_t {fa_last_hip_error()})"
+        super().__init__(msg)
+
+
+def fa_status_str(status: int) -> str:
+    return _lib.lib.fa_status_str(int(status)).decode()
+
+
+def fa_last_hip_error() -> int:
+    return int(_lib.lib.fa_last_hip_error())
+
+
+def fa_decode_workspace_size(B: int, h: int, d_head: int, num_splits: int) -> int:
+    return int(_lib.lib.fa_decode_workspace_size(B, h, d_head, num_splits))
+
+
+def _check_tensor(name, t, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the kernels read raw row-major memory)")
+
+
+def _stream_handle(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes_void(s.cuda_stream)
+
+
+def ctypes_void(x):
+    import ctypes
+    return ctypes.c_void_p(int(x))
+
+
+def _default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def _fwd(entry, out_dtype, q, k, v, causal, scale, o, lse, stream):
+    _check_tensor("q", q, torch.bfloat16, 4)
+    _check_tensor("k", k, torch.bfloat16, 4)
+    _check_tensor("v", v, torch.bfloat16, 4)
+    B, h, Tq, d = q.shape
+    Tk = k.shape[2]
+    if tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    if o is None:
+        o = torch.empty((B, h, Tq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h, Tq), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, out_dtype, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    if tuple(o.shape) != (B, h, Tq, d) or tuple(lse.shape) != (B, h, Tq):
+        raise ValueError("output shapes do not match the inputs")
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+               B, h, Tq, Tk, d, int(bool(causal)), scale, _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def fa_fwd(q, k, v, *, causal: bool, scale: float | None = None, o=None, lse=None, stream=None):
+    """Attention forward.  q [B,h,Tq,d], k/v [B,h,Tk,d] bf16 on the GPU -> (o bf16, lse fp32).
+
+    Enqueued on ``stream`` (default: torch's current stream); outputs are allocated with
+    ``torch.empty`` unless given.  ``scale`` defaults to 1/sqrt(d).
+    """
+    return _fwd(_lib.lib.fa_fwd, torch.bfloat16, q, k, v, causal, scale, o, lse, stream)
+
+
+def fa_fwd_o32(q, k, v, *, causal: bool, scale: float | None = None, o=None, lse=None,
+               stream=None):
+    """Same kernel as :func:`fa_fwd` with an fp32 O (parity diagnostics)."""
+    return _fwd(_lib.lib.fa_fwd_o32, torch.float32, q, k, v, causal, scale, o, lse, stream)
+
+
+def fa_decode(q, k, v, *, num_splits: int, scale: float | None = None, o=None, lse=None,
+              workspace=None, stream=None):
+    """Split-KV decode.  q [B,h,d], k/v [B,h,Tk,d] bf16 -> (o [B,h,d] bf16, lse [B,h] fp32).
+
+    ``workspace`` (a uint8 GPU tensor of at least fa_decode_workspace_size bytes) is allocated
+    with ``torch.empty`` unless given.
+    """
+    _check_tensor("q", q, torch.bfloat16, 3)
+    _check_tensor("k", k, torch.bfloat16, 4)
+    _check_tensor("v", v, torch.bfloat16, 4)
+    B, h, d = q.shape
+    Tk = k.shape[2]
+    if tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o is None:
+        o = torch.empty((B, h, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    need = fa_decode_workspace_size(B, h, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8, 1)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = _lib.lib.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, h, Tk, d, scale, int(num_splits), workspace.data_ptr(),
+                            workspace.numel(), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def fa_validate_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head, causal, scale):
+    """Host-only argument check of the forward entry points (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head,
+                                        int(causal), float(scale)))
+
+
+def fa_validate_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tk, d_head, scale, num_splits,
+                       ws_ptr, ws_bytes):
+    """Host-only argument check of the decode entry point (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tk, d_head,
+                                           float(scale), num_splits, ws_ptr, ws_bytes))

@@ -1,0 +1,57 @@
+// C-ABI entry points: validate on the host, then enqueue the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+thread_local int g_last_hip_error = 0;
+
+int map_hip(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FA_ERR_HIP;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+               int64_t h, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale,
+               void* stream, bool out_f32) {
+  const int st = fa_validate_fwd(q, k, v, o, lse, B, h, Tq, Tk, d, causal, scale);
+  if (st != FA_OK) return st;
+  fa::FwdLaunch a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = static_cast<int>(B); a.H = static_cast<int>(h);
+  a.Tq = static_cast<int>(Tq); a.Tk = static_cast<int>(Tk); a.d = static_cast<int>(d);
+  a.causal = causal != 0; a.out_f32 = out_f32; a.scale = scale;
+  return map_hip(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head, int causal,
+                      float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, h, Tq, Tk, d_head, causal, scale, stream, false);
+}
+
+extern "C" int fa_fwd_o32(const void* q, const void* k, const void* v, float* o, float* lse,
+                          int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                          int causal, float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, h, Tq, Tk, d_head, causal, scale, stream, true);
+}
+
+extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
+                         int64_t num_splits, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const int st = fa_validate_decode(q, k, v, o, lse, B, h, Tk, d_head, scale, num_splits,
+                                    workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::DecodeLaunch a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.workspace = static_cast<float*>(workspace);
+  a.B = static_cast<int>(B); a.H = static_cast<int>(h); a.Tk = static_cast<int>(Tk);
+  a.d = static_cast<int>(d_head); a.num_splits = static_cast<int>(num_splits); a.scale = scale;
+  return map_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa_last_hip_error(void) { return g_last_hip_error; }

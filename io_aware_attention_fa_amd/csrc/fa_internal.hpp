@@ -1,0 +1,35 @@
+// Launch descriptors shared by the host entry points (fa_host.cpp) and the kernel translation
+// units.  Internal to the library; not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Tq, Tk, d;
+  bool causal;
+  bool out_f32;
+  float scale;
+};
+
+struct DecodeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* workspace;
+  int B, H, Tk, d, num_splits;
+  float scale;
+};
+
+hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+}  // namespace fa

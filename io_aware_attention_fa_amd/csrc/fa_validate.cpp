@@ -1,0 +1,83 @@
+// Host-side argument validation, status strings and workspace sizing of the C ABI in fa.h.
+// Pure C++ (no HIP): it runs before any HIP call, so an invalid call enqueues nothing and
+// leaves its outputs untouched.  Compiles with g++ alone for host-only checks.
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool head_dim_ok(int64_t d) { return d == 64 || d == 128; }
+
+// Per-head tensors are addressed with 32-bit byte offsets inside the kernels.
+bool head_bytes_ok(int64_t rows, int64_t d) {
+  // one extra 128-row block of zero-filled reads past the end must still fit in 32 bits
+  return rows <= (FA_MAX_HEAD_BYTES / (2 * d)) - 128;
+}
+
+}  // namespace
+
+extern "C" int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
+                               int64_t d_head, int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_bytes_ok(Tq, d_head) || !head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
+  // the grid is one workgroup per (128-row query block, head, batch) and must fit in 31 bits
+  const int64_t nqb = (Tq + 127) / 128;
+  if (B > INT32_MAX / h || B * h > INT32_MAX / nqb) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Tq > Tk) return FA_ERR_CAUSAL_TQ_GT_TK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+extern "C" size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head,
+                                           int64_t num_splits) {
+  if (B < 1 || h < 1 || d_head < 1 || num_splits < 1) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(h) * static_cast<size_t>(num_splits) *
+         static_cast<size_t>(d_head + 2) * sizeof(float);
+}
+
+extern "C" int fa_validate_decode(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, int64_t B, int64_t h, int64_t Tk,
+                                  int64_t d_head, float scale, int64_t num_splits,
+                                  const void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
+  if (B > 65535 || h > 65535) return FA_ERR_SHAPE;   // grid y / z extents of the split pass
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (num_splits < 1 || num_splits > Tk || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < fa_decode_workspace_size(B, h, d_head, num_splits))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+extern "C" const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is < 1 or exceeds the kernels' limits";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d_head must be 64 or 128";
+    case FA_ERR_CAUSAL_TQ_GT_TK: return "FA_ERR_CAUSAL_TQ_GT_TK: causal attention needs Tq <= Tk";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and causal 0 or 1";
+    case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits must be in [1, min(Tk, FA_MAX_SPLITS)]";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, misaligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed (see fa_last_hip_error)";
+    default: return "unknown fa status code";
+  }
+}

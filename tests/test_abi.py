@@ -1,0 +1,122 @@
+"""The C-ABI library loads and exports every symbol of include/fa.h; host-side validation and
+error behaviour (CPU only: no call here reaches a HIP API)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for name in ("fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size",
+                 "fa_validate_fwd", "fa_validate_decode", "fa_status_str", "fa_last_hip_error"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(fa_lib):
+    exported = subprocess.run(["nm", "-D", "--defined-only", fa_lib.LIB_PATH], capture_output=True,
+                              text=True, check=True).stdout
+    syms = set(re.findall(r"\sT\s+(\w+)$", exported, flags=re.M))
+    for name in header_functions():
+        assert name in syms, f"{name} declared in fa.h but not exported"
+        assert getattr(ctypes.CDLL(fa_lib.LIB_PATH), name)
+
+
+def test_binding_covers_every_declared_function(fa_lib):
+    from io_aware_attention_fa_amd import _lib
+    assert sorted(_lib.SIGNATURES) == header_functions()
+    for name in header_functions():
+        assert callable(getattr(fa_lib, name))
+
+
+def test_status_strings(fa_lib):
+    seen = set()
+    for code in range(0, 10):
+        s = fa_lib.fa_status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in fa_lib.fa_status_str(12345)
+    assert fa_lib.fa_last_hip_error() == 0
+
+
+P = 0x100000   # a 16-byte aligned fake address; validation never dereferences pointers
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, P, P, P, 1, 1, 16, 16, 64, 0, 0.125), 0),
+    ((0, P, P, P, P, 1, 1, 16, 16, 64, 0, 0.125), 1),
+    ((P, P, P, P, 0, 1, 1, 16, 16, 64, 0, 0.125), 1),
+    ((P, P, P, P, P, 0, 1, 16, 16, 64, 0, 0.125), 2),
+    ((P, P, P, P, P, 1, -1, 16, 16, 64, 0, 0.125), 2),
+    ((P, P, P, P, P, 1, 1, 0, 16, 64, 0, 0.125), 2),
+    ((P, P, P, P, P, 1, 1, 16, 0, 64, 0, 0.125), 2),
+    ((P, P, P, P, P, 1, 1, 16, 2**30, 128, 0, 0.125), 2),
+    ((P, P, P, P, P, 1, 1, 16, 16, 96, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 16, 16, 256, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 17, 16, 64, 1, 0.125), 4),
+    ((P, P, P, P, P, 1, 1, 16, 17, 64, 1, 0.125), 0),
+    ((P, P, P, P, P, 1, 1, 17, 16, 64, 0, 0.125), 0),
+    ((P + 8, P, P, P, P, 1, 1, 16, 16, 64, 0, 0.125), 5),
+    ((P, P, P, P, P + 2, 1, 1, 16, 16, 64, 0, 0.125), 5),
+    ((P, P, P, P, P, 1, 1, 16, 16, 64, 0, math.inf), 6),
+    ((P, P, P, P, P, 1, 1, 16, 16, 64, 0, math.nan), 6),
+    ((P, P, P, P, P, 1, 1, 16, 16, 64, 2, 0.125), 6),
+])
+def test_validate_fwd(fa_lib, args, code):
+    assert fa_lib.fa_validate_fwd(*args) == code
+
+
+@pytest.mark.parametrize("B,h,Tk,d,S,ws_delta,code", [
+    (2, 3, 100, 128, 4, 0, 0),
+    (2, 3, 100, 128, 0, 0, 7),
+    (2, 3, 100, 128, 101, 0, 7),
+    (2, 3, 300, 128, 257, 0, 7),
+    (2, 3, 100, 128, 100, 0, 0),
+    (2, 3, 100, 128, 4, -4, 8),
+    (2, 3, 100, 80, 4, 0, 3),
+    (0, 3, 100, 128, 4, 0, 2),
+])
+def test_validate_decode(fa_lib, B, h, Tk, d, S, ws_delta, code):
+    ws = max(fa_lib.fa_decode_workspace_size(max(B, 1), h, d, max(S, 1)) + ws_delta, 0)
+    assert fa_lib.fa_validate_decode(P, P, P, P, P, B, h, Tk, d, 0.1, S, P, ws) == code
+
+
+def test_decode_workspace_size(fa_lib):
+    assert fa_lib.fa_decode_workspace_size(64, 32, 128, 16) == 64 * 32 * 16 * 130 * 4
+    assert fa_lib.fa_decode_workspace_size(0, 32, 128, 16) == 0
+    assert fa_lib.fa_validate_decode(P, P, P, P, P, 1, 1, 10, 64, 0.1, 2, 0, 10**6) == 8
+    assert fa_lib.fa_validate_decode(P, P, P, P, P, 1, 1, 10, 64, 0.1, 2, P + 4, 10**6) == 8
+
+
+def test_invalid_calls_touch_nothing(fa_lib):
+    """Entry points return the validation code before any HIP call; outputs stay untouched.
+
+    Host arrays stand in for device buffers: a rejected call never dereferences them.
+    """
+    from io_aware_attention_fa_amd import _lib
+    buf = np.zeros(4096, dtype=np.uint16)
+    o = np.full(4096, 0x7FC1, dtype=np.uint16)
+    lse = np.full(64, 12345.0, dtype=np.float32)
+    ws = np.full(4096, 7, dtype=np.uint8)
+    a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, o, lse)]
+    st = _lib.lib.fa_fwd(*a, 1, 1, 16, 16, 96, 0, 0.125, None)
+    assert st == 3
+    st = _lib.lib.fa_fwd_o32(*a, 1, 1, 17, 16, 64, 1, 0.125, None)
+    assert st == 4
+    st = _lib.lib.fa_decode(*a, 1, 1, 16, 64, 0.125, 17, ctypes.c_void_p(ws.ctypes.data),
+                            ws.nbytes, None)
+    assert st == 7
+    assert np.all(o == 0x7FC1) and np.all(lse == 12345.0) and np.all(ws == 7)

@@ -1,0 +1,203 @@
+"""GPU parity of the attention forward against the fp64 oracle, through the C ABI.
+
+Gates: max|dO| <= 1e-2 on the kernel's fp32 output (same kernel, fp32 store), max|dLSE| <= 1e-3,
+the bf16 output equal bit-for-bit to the round-to-nearest-even of the fp32 output, and the bf16
+output within 1e-2 plus its own rounding of the oracle.  Full workload sizes run in the launch
+configuration the benchmark times; the oracle checks sampled rows there.
+"""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import attention_ref as ref
+from tests.gpu_support import (LSE_TOL, O_TOL, assert_bf16_is_rne_of_f32, check_rows, log,
+                               run_fwd, to_gpu, workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_rows(q, k, v, wl, heads_rows):
+    """Oracle (O, LSE) for {(b, h): rows}."""
+    out = {}
+    for (b, h), rows in heads_rows.items():
+        out[(b, h)] = ref.naive_attention_head(si.bf16_bits_to_f64(q[b, h]),
+                                               si.bf16_bits_to_f64(k[b, h]),
+                                               si.bf16_bits_to_f64(v[b, h]), wl.scale, wl.causal,
+                                               rows=rows)
+    return out
+
+
+def _check_sampled(tag, res, q, k, v, wl, heads_rows):
+    o32 = res["o32"].cpu().numpy()
+    l32 = res["lse32"].cpu().numpy()
+    o16 = res["o16"].float().cpu().numpy()
+    refs = _oracle_rows(q, k, v, wl, heads_rows)
+    O_ref = np.concatenate([refs[bh][0] for bh in heads_rows])
+    L_ref = np.concatenate([refs[bh][1] for bh in heads_rows])
+    sel = lambda a: np.concatenate([a[b, h][rows] for (b, h), rows in heads_rows.items()])
+    return check_rows(tag, sel(o32), sel(l32), sel(o16), O_ref, L_ref)
+
+
+def test_tiny_noncausal_full(gpu):
+    wl, q, k, v = workload_inputs("tiny_noncausal_b1_h2_t128_d64")
+    res = run_fwd(gpu, q, k, v, wl.causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    heads = {(0, h): np.arange(wl.Tq) for h in range(wl.h)}
+    _check_sampled(wl.name, res, q, k, v, wl, heads)
+
+
+def test_causal_t1024_d64_full_size(gpu):
+    wl, q, k, v = workload_inputs("causal_b8_h32_t1024_d64")
+    res = run_fwd(gpu, q, k, v, wl.causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    rng = np.random.default_rng(11)
+    heads = {(b, h): np.arange(wl.Tq) for b, h in [(0, 0), (3, 17), (7, 31)]}
+    for _ in range(24):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.h))
+        heads.setdefault((b, h), np.sort(rng.choice(wl.Tq, 48, replace=False)))
+    _check_sampled(wl.name, res, q, k, v, wl, heads)
+
+
+def test_causal_t4096_d128_full_size(gpu):
+    wl, q, k, v = workload_inputs("causal_b8_h32_t4096_d128")
+    res = run_fwd(gpu, q, k, v, wl.causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    rng = np.random.default_rng(12)
+    heads = {(5, 9): np.arange(wl.Tq)}
+    edge = np.array([0, 1, 127, 128, 129, 2047, 4094, 4095])
+    for _ in range(16):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.h))
+        rows = np.unique(np.concatenate([edge, rng.choice(wl.Tq, 40, replace=False)]))
+        heads.setdefault((b, h), rows)
+    _check_sampled(wl.name, res, q, k, v, wl, heads)
+
+
+def test_longctx_t16384_keyspikes_full_size(gpu):
+    wl, q, k, v = workload_inputs("longctx_causal_b2_h32_t16384_d128_keyspikes")
+    res = run_fwd(gpu, q, k, v, wl.causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    rng = np.random.default_rng(13)
+    heads = {}
+    edge = np.array([0, 1, 2, 63, 64, 127, 128, 8191, 16382, 16383])
+    for _ in range(12):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.h))
+        rows = np.unique(np.concatenate([edge, rng.choice(wl.Tq, 24, replace=False)]))
+        heads.setdefault((b, h), rows)
+    _check_sampled(wl.name, res, q, k, v, wl, heads)
+
+
+EDGE_SHAPES = [
+    # (B, h, Tq, Tk, d, causal)
+    (1, 1, 1, 1, 64, False), (1, 1, 1, 1, 128, True), (2, 3, 7, 7, 64, True),
+    (1, 2, 63, 63, 128, True), (1, 2, 127, 127, 64, False), (1, 2, 129, 129, 128, True),
+    (2, 2, 1000, 1000, 64, True), (1, 1, 4097, 4097, 128, True), (1, 1, 4097, 4097, 64, False),
+    (2, 2, 100, 333, 128, False), (2, 2, 333, 100, 64, False), (1, 3, 77, 200, 128, True),
+    (1, 2, 1, 513, 128, True), (1, 2, 200, 200, 64, True), (3, 1, 64, 64, 128, True),
+    (1, 1, 65, 1, 64, False), (1, 1, 256, 257, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,h,Tq,Tk,d,causal", EDGE_SHAPES)
+def test_edge_shapes(gpu, B, h, Tq, Tk, d, causal):
+    wl = si.custom_workload(B, h, Tq, Tk, d, causal)
+    q, k, v = si.make_inputs(wl, seed=5, threads=4)
+    res = run_fwd(gpu, q, k, v, causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    heads = {(b, hh): np.arange(Tq) for b in range(B) for hh in range(h)}
+    _check_sampled(f"edge B{B} h{h} Tq{Tq} Tk{Tk} d{d} causal{int(causal)}", res, q, k, v, wl,
+                   heads)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_row_zero_is_exactly_first_value_row(gpu, d):
+    wl = si.custom_workload(2, 4, 300, 300, d, True)
+    q, k, v = si.make_inputs(wl, seed=8, threads=4)
+    res = run_fwd(gpu, q, k, v, True, wl.scale)
+    o16 = res["o16"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(o16[:, :, 0, :], v[:, :, 0, :])
+    qf, kf = si.bf16_bits_to_f64(q), si.bf16_bits_to_f64(k)
+    lse0 = wl.scale * np.einsum("bhd,bhd->bh", qf[:, :, 0], kf[:, :, 0])
+    assert np.max(np.abs(res["lse32"].cpu().numpy()[:, :, 0] - lse0)) <= 1e-5
+
+
+@pytest.mark.parametrize("causal,Tq,Tk", [(True, 300, 300), (True, 100, 357), (False, 130, 257)])
+def test_zero_queries_give_log_count_and_mean(gpu, causal, Tq, Tk):
+    wl = si.custom_workload(1, 2, Tq, Tk, 128, causal)
+    _, k, v = si.make_inputs(wl, seed=9, threads=2)
+    q = np.zeros((1, 2, Tq, 128), dtype=np.uint16)
+    res = run_fwd(gpu, q, k, v, causal, wl.scale)
+    counts = np.arange(Tq) + (Tk - Tq) + 1 if causal else np.full(Tq, Tk)
+    lse = res["lse32"].cpu().numpy()
+    assert np.max(np.abs(lse - np.log(counts)[None, None])) <= LSE_TOL
+    vf = si.bf16_bits_to_f64(v)
+    cum = np.cumsum(vf, axis=2) / np.arange(1, Tk + 1)[None, None, :, None]
+    expect = cum[:, :, counts - 1, :]
+    assert np.max(np.abs(res["o32"].cpu().numpy() - expect)) <= O_TOL
+
+
+def test_constant_values_give_that_constant(gpu):
+    wl = si.custom_workload(1, 2, 200, 200, 64, True)
+    q, k, _ = si.make_inputs(wl, seed=10, threads=2)
+    v = np.full_like(k, si.rne_bf16_bits(np.array([0.375], np.float32))[0])
+    res = run_fwd(gpu, q, k, v, True, wl.scale)
+    # P is rounded to bf16 before the P V contraction while the denominator sums the fp32 p, so
+    # O = c * sum(bf16(p)) / sum(p): within half a bf16 ulp (2^-9 relative) of c, plus fp32 noise.
+    err = np.abs(res["o32"].cpu().numpy() - 0.375)
+    assert np.max(err) <= 0.375 * 2.0 ** -9 + 1e-6
+    assert np.all(err[:, :, 0] == 0.0)   # row 0 sees one key: p = 1 exactly
+
+
+def test_large_scores_stay_finite_and_exact(gpu):
+    """Scores in the hundreds: exp overflows unless the running max is subtracted."""
+    wl = si.custom_workload(1, 2, 256, 256, 128, True)
+    q, k, v = si.make_inputs(wl, seed=14, threads=2)
+    scale = 12.0
+    res = run_fwd(gpu, q, k, v, True, scale)
+    assert torch.isfinite(res["o32"]).all() and torch.isfinite(res["lse32"]).all()
+    heads = {(0, h): np.arange(256) for h in range(2)}
+    refs = {bh: ref.naive_attention_head(si.bf16_bits_to_f64(q[bh]), si.bf16_bits_to_f64(k[bh]),
+                                         si.bf16_bits_to_f64(v[bh]), scale, True)
+            for bh in heads}
+    o32 = res["o32"].cpu().numpy()
+    l32 = res["lse32"].cpu().numpy()
+    for bh in heads:
+        assert np.max(np.abs(o32[bh] - refs[bh][0])) <= O_TOL
+        # |LSE| ~ 1e2 here: allow fp32 relative rounding of the score itself
+        assert np.max(np.abs(l32[bh] - refs[bh][1]) / np.maximum(1, np.abs(refs[bh][1]))) <= LSE_TOL
+
+
+def test_run_to_run_bit_identical(gpu):
+    wl, q, k, v = workload_inputs("causal_b8_h32_t1024_d64")
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+    o1, l1 = gpu.fa_fwd(qg, kg, vg, causal=True, scale=wl.scale)
+    o2, l2 = gpu.fa_fwd(qg, kg, vg, causal=True, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_explicit_stream_and_preallocated_outputs(gpu):
+    wl = si.custom_workload(1, 2, 129, 129, 128, True)
+    q, k, v = si.make_inputs(wl, seed=15, threads=2)
+    qg, kg, vg = to_gpu(q), to_gpu(k), to_gpu(v)
+    s = torch.cuda.Stream()
+    o = torch.empty_like(qg)
+    lse = torch.empty((1, 2, 129), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        gpu.fa_fwd(qg, kg, vg, causal=True, scale=wl.scale, o=o, lse=lse, stream=s)
+    s.synchronize()
+    o_ref, l_ref = gpu.fa_fwd(qg, kg, vg, causal=True, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref)
+
+
+def test_rejected_call_leaves_device_outputs_untouched(gpu):
+    qg = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((1, 1, 16, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((1, 1, 16), 7.0, device="cuda")
+    kg = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu.FaError) as e:
+        gpu.fa_fwd(qg, kg, kg, causal=True, scale=0.125, o=o, lse=lse)   # causal with Tq > Tk
+    assert e.value.status == gpu.FA_ERR_CAUSAL_TQ_GT_TK
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0) and torch.all(lse == 7.0)
