@@ -65,6 +65,21 @@ def build_library(verbose: bool = False) -> str:
     tmp = out + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
+    build_calibration(verbose)
+    return out
+
+
+def calibration_library_path() -> str:
+    return os.path.join(PKG, "libfa_calib.so")
+
+
+def build_calibration(verbose: bool = False) -> str:
+    """The gfx950 calibration microbenchmarks (libfa_calib.so, see calibrate.py)."""
+    out = calibration_library_path()
+    tmp = out + ".tmp"
+    _run([_hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, "-shared", "-x", "hip",
+          os.path.join(PKG, "calib", "fa_calib.hip"), "-o", tmp], verbose)
+    os.replace(tmp, out)
     return out
 
 

@@ -1,0 +1,143 @@
+// Calibration microbenchmarks for gfx950: the ceilings the attention kernels run against.
+//   mfma   : dense bf16 v_mfma_f32_32x32x16_bf16 throughput (8 independent accumulators / wave)
+//   exp    : v_exp_f32 throughput (16 independent chains / lane, x <- 2^-x stays in [0.5, 1])
+//   lds    : ds_read_b128 and ds_read_b64_tr_b16 bandwidth (conflict-free addresses)
+//   hbm    : streaming read of a large buffer with 16-byte buffer loads
+//   clock  : shader clock from s_memtime against the 100 MHz s_memrealtime counter
+// Every kernel reads and writes only inside the buffers it is given.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_mfma(float* out, int iters) {
+  const int l = threadIdx.x;
+  bf16x8_t a, b;
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(0.001f * (l + j));
+    b[j] = (__bf16)(0.002f * (l - j));
+  }
+  f32x16_t c[8];
+  for (int i = 0; i < 8; ++i) c[i] = f32x16_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  out[blockIdx.x * blockDim.x + l] = s;
+}
+
+__global__ __launch_bounds__(256) void k_exp(float* out, int iters) {
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = 0.5f + 0.01f * i + 1e-6f * threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// LDS: 64 KB per workgroup; lane l of wave w reads 16 bytes at ((w*64 + l + 64*k) * 16) mod 64 KB.
+__global__ __launch_bounds__(256) void k_lds_b128(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t sm[16384];
+  for (int i = threadIdx.x; i < 16384; i += 256) sm[i] = i * 2654435761u;
+  __syncthreads();
+  uint32_t acc0 = 0, acc1 = 0;
+  const uint32_t base = threadIdx.x * 16u;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t addr = (base + (uint32_t)k * 4096u + (uint32_t)it * 64u) & 0xFFF0u;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(sm) + addr);
+      acc0 = acc0 ^ v[0] ^ v[1];
+      acc1 = acc1 ^ v[2] ^ v[3];
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc0 + acc1;
+}
+
+__global__ __launch_bounds__(256) void k_lds_tr(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint16_t sm[32768];
+  for (int i = threadIdx.x; i < 32768; i += 256) sm[i] = (uint16_t)(i * 40503u);
+  __syncthreads();
+  typedef __attribute__((address_space(3))) s16x4_t* lp;
+  uint32_t acc = 0;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      // element offset: 16 rows x 64 elements tile, 8-byte chunks, inside 32768 elements
+      const uint32_t e = ((lane % 16) * 64 + (lane / 16) * 4 + wave * 1024 + k * 4096 +
+                          (uint32_t)(it & 3) * 16) & 32767u;
+      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(sm + e));
+      acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[3] << 16);
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// Streaming read: thread t reads 16-byte chunks t, t + stride, ... of n16 chunks.
+__global__ __launch_bounds__(256) void k_hbm_read(const u32x4_t* __restrict__ src, long n16,
+                                                  uint32_t* out) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = __builtin_nontemporal_load(src + i);
+    const u32x4_t b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= a[0] ^ b[1] ^ c[2] ^ d[3] ^ a[3] ^ b[2] ^ c[1] ^ d[0];
+  }
+  for (; i < n16; i += stride) acc ^= src[i][0];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ void k_clock(unsigned long long* out, int spin) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  float x = threadIdx.x;
+  for (int i = 0; i < spin; ++i) x = __builtin_fmaf(x, 0.999999f, 1e-7f);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = t1 - t0;
+    out[1] = r1 - r0;
+    out[2] = (unsigned long long)(x > 1e30f);
+  }
+}
+
+extern "C" {
+int calib_mfma(float* out, int blocks, int iters, void* s) {
+  hipLaunchKernelGGL(k_mfma, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+  return (int)hipGetLastError();
+}
+int calib_exp(float* out, int blocks, int iters, void* s) {
+  hipLaunchKernelGGL(k_exp, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+  return (int)hipGetLastError();
+}
+int calib_lds_b128(uint32_t* out, int blocks, int iters, void* s) {
+  hipLaunchKernelGGL(k_lds_b128, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+  return (int)hipGetLastError();
+}
+int calib_lds_tr(uint32_t* out, int blocks, int iters, void* s) {
+  hipLaunchKernelGGL(k_lds_tr, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+  return (int)hipGetLastError();
+}
+int calib_hbm_read(const void* src, long n16, uint32_t* out, int blocks, void* s) {
+  hipLaunchKernelGGL(k_hbm_read, dim3(blocks), dim3(256), 0, (hipStream_t)s,
+                     (const u32x4_t*)src, n16, out);
+  return (int)hipGetLastError();
+}
+int calib_clock(unsigned long long* out, int spin, void* s) {
+  hipLaunchKernelGGL(k_clock, dim3(1), dim3(64), 0, (hipStream_t)s, out, spin);
+  return (int)hipGetLastError();
+}
+}

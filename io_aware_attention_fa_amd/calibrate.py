@@ -1,0 +1,77 @@
+"""Run the gfx950 calibration microbenchmarks (libfa_calib.so) and print one JSON object.
+
+Measures the ceilings the attention kernels are held against: dense bf16 MFMA FLOP/s, v_exp_f32
+rate, LDS read bandwidth (ds_read_b128 and ds_read_b64_tr_b16), streaming HBM read bandwidth and
+the shader clock.  Usage: python -m io_aware_attention_fa_amd.calibrate
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+import torch
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_calib.so")
+
+
+def _time(fn, reps=5):
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps * 1e-3
+
+
+def main():
+    lib = ctypes.CDLL(LIB)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"device": torch.cuda.get_device_properties(0).name, "cus": cus}
+
+    clk = torch.zeros(3, dtype=torch.int64, device="cuda")
+    lib.calib_clock(ctypes.c_void_p(clk.data_ptr()), 2_000_000, st)
+    torch.cuda.synchronize()
+    c = clk.cpu().tolist()
+    res["sclk_mhz_from_memtime"] = c[0] / c[1] * 100.0 if c[1] else None
+
+    blocks = cus * 8
+    out = torch.empty(cus * 16 * 256, dtype=torch.float32, device="cuda")
+    iters = 4000
+    t = _time(lambda: lib.calib_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, st))
+    res["mfma_bf16_tflops"] = blocks * 4 * iters * 8 * 32768 / t / 1e12
+
+    iters = 20000
+    t = _time(lambda: lib.calib_exp(ctypes.c_void_p(out.data_ptr()), blocks, iters, st))
+    res["exp2_per_s"] = blocks * 256 * iters * 16 / t
+
+    outu = out.view(torch.int32)
+    blocks_l = cus * 2
+    iters = 20000
+    t = _time(lambda: lib.calib_lds_b128(ctypes.c_void_p(outu.data_ptr()), blocks_l, iters, st))
+    bps = blocks_l * 256 * iters * 8 * 16 / t
+    res["lds_b128_bytes_per_s"] = bps
+    res["lds_b128_bytes_per_clk_per_cu_at_2400"] = bps / cus / 2.4e9
+    t = _time(lambda: lib.calib_lds_tr(ctypes.c_void_p(outu.data_ptr()), blocks_l, iters, st))
+    bps = blocks_l * 256 * iters * 8 * 8 / t
+    res["lds_tr16_b64_bytes_per_s"] = bps
+    res["lds_tr16_b64_bytes_per_clk_per_cu_at_2400"] = bps / cus / 2.4e9
+
+    n = 4 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    for blocks_h in (cus * 4, cus * 8, cus * 16):
+        t = _time(lambda: lib.calib_hbm_read(ctypes.c_void_p(src.data_ptr()), n // 16,
+                                             ctypes.c_void_p(outu.data_ptr()), blocks_h, st))
+        res[f"hbm_read_GBps_blocks{blocks_h}"] = n / t / 1e9
+    dst = torch.empty_like(src)
+    t = _time(lambda: dst.copy_(src))
+    res["torch_copy_GBps_read_plus_write"] = 2 * n / t / 1e9
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()
