@@ -26,9 +26,11 @@
  *     launch returns FA_ERR_HIP; fa_last_hip_error() then gives the hipError_t (per thread).
  *     No C++ exception crosses this interface.
  *   - Thread safety: the library holds no state besides the per-thread last HIP error.
- *   - Precision: bf16 inputs, fp32 accumulation of both contractions and of the softmax state,
- *     P rounded to bf16 (round to nearest even) before the P V contraction, O rounded to bf16
- *     (round to nearest even) at the end, LSE in fp32.
+ *   - Precision: bf16 inputs, fp32 accumulation of both contractions and of the softmax state.
+ *     In fa_fwd, P is rounded to bf16 (round to nearest even) for the P V contraction and O is
+ *     divided by the fp32 sum of those rounded values (so O is a convex combination of the V
+ *     rows); the LSE uses the fp32 sum of the unrounded p.  fa_decode keeps p in fp32
+ *     throughout.  O is rounded to bf16 (round to nearest even) at the end; LSE is fp32.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

@@ -13,23 +13,35 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void k_mfma(float* out, int iters) {
+// NACC independent accumulator chains per wave; wave 0 of block 0 records the shader clock
+// (s_memtime) and the 100 MHz reference (s_memrealtime) around its loop.
+template <int NACC>
+__global__ __launch_bounds__(256) void k_mfma(float* out, int iters, unsigned long long* clk) {
   const int l = threadIdx.x;
   bf16x8_t a, b;
   for (int j = 0; j < 8; ++j) {
     a[j] = (__bf16)(0.001f * (l + j));
     b[j] = (__bf16)(0.002f * (l - j));
   }
-  f32x16_t c[8];
-  for (int i = 0; i < 8; ++i) c[i] = f32x16_t{};
+  f32x16_t c[NACC];
+  for (int i = 0; i < NACC; ++i) c[i] = f32x16_t{};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+    for (int i = 0; i < NACC; ++i)
+      c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
   }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   float s = 0.f;
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NACC; ++i)
     for (int j = 0; j < 16; ++j) s += c[i][j];
   out[blockIdx.x * blockDim.x + l] = s;
+  if (blockIdx.x == 0 && l == 0) {
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_exp(float* out, int iters) {
@@ -38,6 +50,40 @@ __global__ __launch_bounds__(256) void k_exp(float* out, int iters) {
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// VALU throughput of one opcode: 16 independent chains per lane.
+//   op 0: v_add_f32, 1: v_fma_f32, 2: v_dot2c_f32_bf16, 3: v_cvt_pk_bf16_f32 (+ v_add to chain),
+//   4: v_max3_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int OP>
+__global__ __launch_bounds__(256) void k_valu(float* out, int iters) {
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = 0.5f + 0.01f * i + 1e-6f * threadIdx.x;
+  const float c = 1.0000001f, d = -0.0000001f;
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (OP == 0) x[i] = x[i] + d;
+      if (OP == 1) x[i] = __builtin_fmaf(x[i], c, d);
+      if (OP == 2) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, x[i]) & 0x3F803F80u;
+        x[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u), ones, x[i], false);
+      }
+      if (OP == 3) {
+        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        f2 f = {x[i], x[(i + 1) & 15]};
+        bf16x2v h = __builtin_convertvector(f, bf16x2v);
+        x[i] = __builtin_bit_cast(float, h);
+      }
+      if (OP == 4) x[i] = fmaxf(fmaxf(x[i], x[(i + 1) & 15]), x[(i + 2) & 15]) * c;
+    }
   }
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += x[i];
@@ -115,12 +161,29 @@ __global__ void k_clock(unsigned long long* out, int spin) {
 }
 
 extern "C" {
-int calib_mfma(float* out, int blocks, int iters, void* s) {
-  hipLaunchKernelGGL(k_mfma, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+int calib_mfma(float* out, int blocks, int iters, int nacc, unsigned long long* clk, void* s) {
+  const hipStream_t st = (hipStream_t)s;
+  switch (nacc) {
+    case 1: hipLaunchKernelGGL(k_mfma<1>, dim3(blocks), dim3(256), 0, st, out, iters, clk); break;
+    case 2: hipLaunchKernelGGL(k_mfma<2>, dim3(blocks), dim3(256), 0, st, out, iters, clk); break;
+    case 4: hipLaunchKernelGGL(k_mfma<4>, dim3(blocks), dim3(256), 0, st, out, iters, clk); break;
+    default: hipLaunchKernelGGL(k_mfma<8>, dim3(blocks), dim3(256), 0, st, out, iters, clk); break;
+  }
   return (int)hipGetLastError();
 }
 int calib_exp(float* out, int blocks, int iters, void* s) {
   hipLaunchKernelGGL(k_exp, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
+  return (int)hipGetLastError();
+}
+int calib_valu(float* out, int blocks, int iters, int op, void* s) {
+  const hipStream_t st = (hipStream_t)s;
+  switch (op) {
+    case 0: hipLaunchKernelGGL(k_valu<0>, dim3(blocks), dim3(256), 0, st, out, iters); break;
+    case 1: hipLaunchKernelGGL(k_valu<1>, dim3(blocks), dim3(256), 0, st, out, iters); break;
+    case 2: hipLaunchKernelGGL(k_valu<2>, dim3(blocks), dim3(256), 0, st, out, iters); break;
+    case 3: hipLaunchKernelGGL(k_valu<3>, dim3(blocks), dim3(256), 0, st, out, iters); break;
+    default: hipLaunchKernelGGL(k_valu<4>, dim3(blocks), dim3(256), 0, st, out, iters); break;
+  }
   return (int)hipGetLastError();
 }
 int calib_lds_b128(uint32_t* out, int blocks, int iters, void* s) {

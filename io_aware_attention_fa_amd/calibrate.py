@@ -39,15 +39,28 @@ def main():
     c = clk.cpu().tolist()
     res["sclk_mhz_from_memtime"] = c[0] / c[1] * 100.0 if c[1] else None
 
-    blocks = cus * 8
     out = torch.empty(cus * 16 * 256, dtype=torch.float32, device="cuda")
-    iters = 4000
-    t = _time(lambda: lib.calib_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, st))
-    res["mfma_bf16_tflops"] = blocks * 4 * iters * 8 * 32768 / t / 1e12
+    for waves_per_simd, nacc in ((2, 1), (2, 2), (2, 4), (2, 8), (1, 2), (1, 4), (1, 8)):
+        blocks = cus * waves_per_simd
+        iters = 32000 // nacc
+        t = _time(lambda: lib.calib_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, nacc,
+                                         ctypes.c_void_p(clk.data_ptr()), st))
+        c = clk.cpu().tolist()
+        res[f"mfma_bf16_tflops_{waves_per_simd}wave_{nacc}acc"] = (
+            blocks * 4 * iters * nacc * 32768 / t / 1e12)
+        res[f"mfma_sclk_mhz_{waves_per_simd}wave_{nacc}acc"] = c[0] / c[1] * 100.0 if c[1] else None
 
+    blocks = cus * 8
     iters = 20000
     t = _time(lambda: lib.calib_exp(ctypes.c_void_p(out.data_ptr()), blocks, iters, st))
     res["exp2_per_s"] = blocks * 256 * iters * 16 / t
+
+    for op, name in enumerate(("add_f32", "fma_f32", "dot2c_f32_bf16", "cvt_pk_bf16_f32",
+                               "max3_f32")):
+        t = _time(lambda: lib.calib_valu(ctypes.c_void_p(out.data_ptr()), blocks, iters, op, st))
+        # wave-instructions per CU per clock at 2.4 GHz (4 SIMDs: 4.0 = one per SIMD per clock)
+        insts = blocks * 4 * iters * 16
+        res[f"valu_{name}_wave_insts_per_clk_per_cu"] = insts / t / cus / 2.4e9
 
     outu = out.view(torch.int32)
     blocks_l = cus * 2

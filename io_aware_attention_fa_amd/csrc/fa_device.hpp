@@ -7,6 +7,7 @@ namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -14,6 +15,10 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// (1.0, 1.0) in bf16: a v_dot2 against it sums a bf16 pair in fp32.
+__device__ __forceinline__ bf16x2_t ones_bf16x2() {
+  return __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+}
 
 // Buffer resource over [base, base + bytes): loads at byte offsets >= bytes return zeros, which
 // gives free, fault-free handling of ragged tails.  Word 3 selects 32-bit raw dword data.
@@ -35,6 +40,11 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Scalar helpers take their operand by value: this compiler mis-lowers a bit cast applied
+// directly to a subscripted vector element (it reads element 0), so never write
+// __builtin_bit_cast(T, vec[i]).
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);

@@ -1,4 +1,4 @@
-// Attention forward (prefill) for gfx950: one workgroup per (128-row query block, head, batch).
+// Attention forward (prefill) for gfx950: one workgroup per (256-row query block, head, batch).
 //
 // The method (page "Fusion and IO-aware kernels", "How it really works", FlashAttention steps
 // 1-4; page "Kernels -- fusion and FlashAttention", sections 3-5): a block of query rows stays
@@ -7,21 +7,32 @@
 // LSE = m + ln l.  The score tile never leaves registers.
 //
 // MI355X mapping (our design, not the pages'):
-//   * 4 waves x 32 query rows = 128 rows per workgroup; key tiles of 64 rows.
+//   * 8 waves x 32 query rows = 256 rows per workgroup, two waves per SIMD; key tiles of 64.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the Q
 //     fragment is the B operand and lives in registers for the whole kernel, K is the A operand
 //     read from LDS.  In the MFMA output layout every lane then owns ONE query row (lane % 32)
 //     and 16 of the tile's keys per 32-key block, so the row max and row sum are in-lane
-//     reductions plus one exchange with lane ^ 32.
+//     reductions plus one exchange with lane ^ 32 (v_permlane32_swap).
 //   * The P V contraction is also computed transposed, O^T += V^T P^T: P^T comes straight from
 //     the score registers (rounded to bf16) as the B operand, V^T is the A operand read from
-//     LDS.  For that, V is transposed while it is staged into LDS, with its key columns
-//     permuted so that the 8 keys a lane holds in P are 8 adjacent LDS columns.
-//   * The output accumulator (d x 32 rows per wave) stays in registers; the per-row rescale
-//     by exp(m_old - m_new) is an in-lane multiply.
-//   * exp is computed as exp2 with scale * log2(e) folded into one multiply-add per score.
-//   * K/V tiles are double-buffered in LDS: the next tile's global loads are issued before the
-//     current tile's math, and written to the other LDS buffer after it (one barrier per tile).
+//     LDS.  V is transposed while it is staged into LDS, with its key columns permuted so that
+//     the 8 keys a lane holds in P are 8 adjacent LDS columns.
+//   * Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the four SIMDs pairwise and run
+//     the same program half a step apart.  Each step is a matrix section (this tile's S^T and
+//     the previous tile's O^T, 32 MFMAs, issued at raised priority) followed by a vector section
+//     (online softmax of this tile and staging of a later K/V tile into LDS), each closed by a
+//     workgroup barrier; group B starts one section late, so on every SIMD one wave feeds the
+//     matrix core while the other runs the exp/max/sum work.
+//   * K/V tiles live in a 4-deep ring of LDS stages (4 x 35 KB): tile t+3 is loaded into one of
+//     two register sets in matrix section t and written to LDS in vector section t+1.
+//   * Online softmax in log2 units with scale * log2(e) folded into one fused multiply-add per
+//     score; the row max is taken on the raw scores.  P is rounded to bf16 for the O^T MFMA and
+//     O is normalised by the sum of those rounded values (a v_dot2 against (1, 1) per pair), so
+//     O is an exact convex combination of the V rows the MFMA used; the LSE takes the sum of
+//     the fp32 p.  The rescale of the accumulator by
+//     exp(m_old - m_new) is skipped (one wave-uniform branch) unless some row's max has grown by
+//     more than 2^8 since the last rescale: stale maxima only scale p, l and acc by the same
+//     factor (at most 256), so O = acc / l and LSE = m + log l are unchanged.
 //   * Buffer loads with a per-head range return zeros past the end of Q/K/V, so ragged tails
 //     need only the -inf score mask (page "Chapter 10 Writing and Benchmarking Custom
 //     Kernels", section 10.3.1, "What You Actually Decide in Practice": the final partial tile).
@@ -32,15 +43,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kBN = 64;       // keys per tile
-constexpr int kThreads = 256;
+constexpr int kBM = 256;       // query rows per workgroup
+constexpr int kBN = 64;        // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;     // LDS ring depth
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 struct FwdParams {
   const uint16_t* q;
@@ -49,7 +65,8 @@ struct FwdParams {
   void* o;
   float* lse;
   int Tq, Tk, nqb, total_wg;
-  float scale_log2;
+  float scale_log2;   // |scale| * log2(e), > 0
+  uint32_t q_sign;    // 0x80008000 when scale < 0 (Q is negated instead), else 0
 };
 
 // Column of the V^T tile that holds key c (an involution): inside each group of 16 keys the
@@ -70,14 +87,15 @@ struct Tile {
   static constexpr int VELEMS = D * VSTR;
   static constexpr int STAGE = KELEMS + VELEMS;
   static constexpr int KCHUNKS = kBN * D / 8 / kThreads;   // 16-byte K chunks per thread
-  static constexpr int VPAIRS = 16 * (D / 8);              // (4-key group, 8-d chunk) pairs
+  static constexpr int VPAIRS = 32 * (D / 8);              // (2-key group, 8-d chunk) pairs
+  static_assert(KCHUNKS >= 1 && VPAIRS <= kThreads, "staging layout");
 };
 
-// Global -> registers for one K/V tile starting at key j0.
+// Global -> registers: this thread's share of the K/V tile starting at key j0.
 template <int D>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           int j0, int tid, u32x4_t (&kr)[Tile<D>::KCHUNKS],
-                                          u32x4_t (&vr)[4]) {
+                                          u32x4_t (&vr)[2]) {
 #pragma unroll
   for (int it = 0; it < Tile<D>::KCHUNKS; ++it) {
     const int c = tid + kThreads * it;
@@ -85,10 +103,10 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_bu
     kr[it] = buf_load16(rk, (uint32_t)((j0 + row) * D + col8 * 8) * 2u);
   }
   if (tid < Tile<D>::VPAIRS) {
-    const int kg = tid & 15, dc = tid >> 4;
+    const int kg = tid & 31, dc = tid >> 5;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vr[r] = buf_load16(rv, (uint32_t)((j0 + 4 * kg + r) * D + dc * 8) * 2u);
+    for (int r = 0; r < 2; ++r)
+      vr[r] = buf_load16(rv, (uint32_t)((j0 + 2 * kg + r) * D + dc * 8) * 2u);
   }
 }
 
@@ -96,7 +114,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_bu
 template <int D>
 __device__ __forceinline__ void store_tile(uint16_t* stage, int tid,
                                            const u32x4_t (&kr)[Tile<D>::KCHUNKS],
-                                           const u32x4_t (&vr)[4]) {
+                                           const u32x4_t (&vr)[2]) {
   using T = Tile<D>;
 #pragma unroll
   for (int it = 0; it < T::KCHUNKS; ++it) {
@@ -105,29 +123,50 @@ __device__ __forceinline__ void store_tile(uint16_t* stage, int tid,
     *reinterpret_cast<u32x4_t*>(stage + row * T::KSTR + col8 * 8) = kr[it];
   }
   if (tid < T::VPAIRS) {
-    const int kg = tid & 15, dc = tid >> 4;
-    uint16_t* vt = stage + T::KELEMS + vt_col(4 * kg);
+    const int kg = tid & 31, dc = tid >> 5;
+    uint16_t* vt = stage + T::KELEMS + vt_col(2 * kg);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      const int w = dd >> 1;
-      u32x2_t pk;
-      pk[0] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);   // keys 4kg, 4kg+1
-      pk[1] = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);   // keys 4kg+2, 4kg+3
-      *reinterpret_cast<u32x2_t*>(vt + (dc * 8 + dd) * T::VSTR) = pk;
+      *reinterpret_cast<uint32_t*>(vt + (dc * 8 + dd) * T::VSTR) =
+          __builtin_amdgcn_perm(vr[1][dd >> 1], vr[0][dd >> 1], sel);   // keys 2kg, 2kg+1
     }
   }
 }
 
+// A lane's value and the value of lane l ^ 32.  With both operands holding v,
+// v_permlane32_swap leaves lanes 0-31 with (v[l], v[l+32]) and lanes 32-63 with (v[l-32], v[l]).
+// The two halves of the result are copied into named scalars before use: reading them through
+// a bit cast of the subscripted result made this compiler substitute half 0 for half 1.
+__device__ __forceinline__ void xhalf_pair(float v, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t s0 = s[0], s1 = s[1];
+  a = __builtin_bit_cast(float, s0);
+  b = __builtin_bit_cast(float, s1);
+}
+__device__ __forceinline__ float xhalf_max(float v) {
+  float a, b;
+  xhalf_pair(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  float a, b;
+  xhalf_pair(v, a, b);
+  return a + b;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
   constexpr int NS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int ND = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * T::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
+  const bool group_b = wave >= 4;
 
   // ---- workgroup -> (batch*head, query block) ----
   const int n = blockIdx.x;
@@ -153,118 +192,188 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool wave_has_rows = qw0 < p.Tq;
   bf16x8_t qf[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qf[s] = as_bf16x8(buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u));
+  for (int s = 0; s < NS; ++s) {
+    u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
+    w ^= p.q_sign;
+    qf[s] = as_bf16x8(w);
+  }
 
   // keys the workgroup needs: all, or (causal) up to the block's last row
   int kend = p.Tk;
   if (CAUSAL) kend = min(p.Tk, min(i0 + kBM, p.Tq) + off);
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  float m_run = -INFINITY;   // running max, log2 units (scores * scale * log2 e)
-  float l_run = 0.f;         // this lane's partial running denominator
+  auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
+
+  float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
+  float l_run = 0.f;         // this lane's partial running sum of p (fp32): the LSE
+  float l16_run = 0.f;       // this lane's partial running sum of bf16(p): normalises O
   f32x16_t oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x16_t{};
+  f32x16_t sacc[2];
+  bf16x8_t pb[4];
 
-  u32x4_t kr[T::KCHUNKS], vr[4];
-  load_tile<D>(rk, rv, 0, tid, kr, vr);
-  store_tile<D>(lds, tid, kr, vr);
+  // ---- prologue: tiles 0 and 1 into stages 0 and 1 ----
+  // Two register sets stage K/V tiles on their way to LDS: tile x uses set x % 2.  Tile t+3 is
+  // loaded in matrix section t and written to LDS in vector section t+1, so a global load has
+  // two sections to land.
+  u32x4_t kr0[T::KCHUNKS], vr0[2], kr1[T::KCHUNKS], vr1[2];
+  load_tile<D>(rk, rv, 0, tid, kr0, vr0);
+  store_tile<D>(lds, tid, kr0, vr0);
+  if (ntiles > 1) {
+    load_tile<D>(rk, rv, kBN, tid, kr1, vr1);
+    store_tile<D>(lds + T::STAGE, tid, kr1, vr1);
+  }
+  if (ntiles > 2) load_tile<D>(rk, rv, 2 * kBN, tid, kr0, vr0);
   __syncthreads();
+  if (group_b) __syncthreads();   // group B runs one section behind group A
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kBN;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile<D>(rk, rv, j0 + kBN, tid, kr, vr);
-
-    const bool active = wave_has_rows && !(CAUSAL && j0 > qw_last + off);
-    if (active) {
-      const uint16_t* ks = lds + (t & 1) * T::STAGE;
-      const uint16_t* vt = ks + T::KELEMS;
-
-      // S^T block kb: keys j0 + 32kb + [0, 32) x this wave's 32 queries
-      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+  auto step = [&](const int t, auto parity) {
+    constexpr int P = decltype(parity)::value;   // == t % 2
+    auto& kr_store = P ? kr1 : kr0;   // tile t+2
+    auto& vr_store = P ? vr1 : vr0;
+    auto& kr_load = P ? kr0 : kr1;    // tile t+3
+    auto& vr_load = P ? vr0 : vr1;
+    // ================= matrix section =================
+    __builtin_amdgcn_s_setprio(1);
+    if (t + 3 < ntiles) load_tile<D>(rk, rv, (t + 3) * kBN, tid, kr_load, vr_load);
+    {
+      // Operands stream through a ring of kRing LDS reads issued ahead of the MFMAs that use
+      // them: first the 2*NS K operands of S^T = K Q^T, then the 4*ND V^T operands of
+      // O^T += V^T P^T.  The three cases (both products, S^T only on the first tile, O^T only
+      // after the last) are separate compile-time instances so every ring index is static.
+      constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
+      const uint16_t* ks = lds + (t % kStages) * T::STAGE + r32 * T::KSTR + 8 * g;
+      const uint16_t* vt = lds + ((t + kStages - 1) % kStages) * T::STAGE + T::KELEMS +
+                           r32 * T::VSTR + 8 * g;
+      // operand i < NK: K rows 32*(i%2) + r32, d 16*(i/2) + 8g; i >= NK: V^T rows
+      // 32*(j%ND) + r32, keys 16*(j/ND) + 8g with j = i - NK.
+      auto opnd = [&](int i) -> bf16x8_t {
+        if (i < NK)
+          return *reinterpret_cast<const bf16x8_t*>(ks + (32 * (i & 1)) * T::KSTR + 16 * (i >> 1));
+        const int j = i - NK;
+        return *reinterpret_cast<const bf16x8_t*>(vt + (32 * (j % ND)) * T::VSTR + 16 * (j / ND));
+      };
+      auto section = [&](auto with_s, auto with_o) {
+        constexpr int first = decltype(with_s)::value ? 0 : NK;
+        constexpr int last = decltype(with_o)::value ? NK + NV : NK;
+        bf16x8_t ring[kRing];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              ks + (32 * kb + r32) * T::KSTR + 16 * s + 8 * g);
-          sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+        for (int i = 0; i < kRing; ++i)
+          if (first + i < last) ring[i] = opnd(first + i);
+        if (decltype(with_s)::value) {
+          sacc[0] = f32x16_t{};
+          sacc[1] = f32x16_t{};
         }
-      }
-
-      // ---- online softmax for this lane's query row ----
-      float x[32];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int i = first; i < last; ++i) {
+          const bf16x8_t a = ring[(i - first) % kRing];
+          if (i + kRing < last) ring[(i - first) % kRing] = opnd(i + kRing);
+          if (i < NK) {
+            sacc[i & 1] = mfma_32x32x16(a, qf[i >> 1], sacc[i & 1]);
+          } else {
+            const int j = i - NK;
+            oacc[j % ND] = mfma_32x32x16(a, pb[j / ND], oacc[j % ND]);
+          }
+        }
+        // keep kRing LDS reads in flight: kRing reads, then (MFMA, read) pairs, then MFMAs
+        constexpr int n = last - first;
+        constexpr int ahead = n < kRing ? n : kRing;
+        __builtin_amdgcn_sched_group_barrier(0x100, ahead, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[kb * 16 + i] = sacc[kb][i] * p.scale_log2;
+        for (int i = 0; i < n - ahead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
+      };
+      const bool do_s = t < ntiles && active(t);
+      const bool do_o = t >= 1 && active(t - 1);
+      using yes = std::true_type;
+      using no = std::false_type;
+      if (do_s && do_o) section(yes{}, yes{});
+      else if (do_s) section(yes{}, no{});
+      else if (do_o) section(no{}, yes{});
+    }
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
 
-      const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+    // ================= vector section =================
+    if (t < ntiles) {
+      if (active(t)) {
+        const int j0 = t * kBN;
+        const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
+        if (need_mask) {
+          const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key > lim) sacc[kb][i] = -INFINITY;
+            }
+        }
+        float mt = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int i = 2; i < 16; ++i) mt = fmaxf(mt, sacc[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
+        mt = xhalf_max(mt) * p.scale_log2;
+        // lazy rescale: only when some row's max outgrew the max in use by > 2^8
+        if (__any(mt > m_run + kRescaleThreshold)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float corr = fast_exp2(m_run - m_new);
+          l_run *= corr;
+          l16_run *= corr;
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+          m_run = m_new;
+        }
+        float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > lim) x[kb * 16 + i] = -INFINITY;
+            const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
+            sacc[kb][i] = e;
+            psum += e;
           }
-      }
-
-      float mt = x[0];
+        l_run += psum;
+        // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
 #pragma unroll
-      for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);   // finite: key 0 is visible to every row
-      const float corr = fast_exp2(m_run - m_new);
-      float psum = 0.f;
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x16_t& sb = sacc[ks >> 1];
+          const int b0 = (ks & 1) * 8;
+          const u32x2_t lo = pack_bf16x4(sb[b0], sb[b0 + 1], sb[b0 + 2], sb[b0 + 3]);
+          const u32x2_t hi = pack_bf16x4(sb[b0 + 4], sb[b0 + 5], sb[b0 + 6], sb[b0 + 7]);
+          u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+          pb[ks] = as_bf16x8(w);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        x[i] = fast_exp2(x[i] - m_new);
-        psum += x[i];
-      }
-      l_run = l_run * corr + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-
-      // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
-      bf16x8_t pb[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int base = (ks >> 1) * 16 + (ks & 1) * 8;
-        u32x4_t w;
-        const u32x2_t lo = pack_bf16x4(x[base], x[base + 1], x[base + 2], x[base + 3]);
-        const u32x2_t hi = pack_bf16x4(x[base + 4], x[base + 5], x[base + 6], x[base + 7]);
-        w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
-        pb[ks] = as_bf16x8(w);
-      }
-
-      // O^T block db: d rows 32db + [0, 32) x this wave's 32 queries
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              vt + (32 * db + r32) * T::VSTR + 16 * ks + 8 * g);
-          oacc[db] = mfma_32x32x16(a, pb[ks], oacc[db]);
+          for (int e = 0; e < 4; ++e)
+            l16_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]),
+                                                      ones_bf16x2(), l16_run, false);
         }
       }
+      if (t + 2 < ntiles)
+        store_tile<D>(lds + ((t + 2) % kStages) * T::STAGE, tid, kr_store, vr_store);
     }
-
-    if (has_next) store_tile<D>(lds + ((t + 1) & 1) * T::STAGE, tid, kr, vr);
     __syncthreads();
+  };
+  for (int t = 0; t <= ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (!group_b) __syncthreads();   // match group B's extra barrier
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ----
   if (!wave_has_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
+  const float l16_tot = xhalf_sum(l16_run);
   if (qrow >= p.Tq) return;
-  const float inv = 1.0f / l_tot;
+  const float inv = 1.0f / l16_tot;
   const size_t orow = qbase + (size_t)qrow * D;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
@@ -297,7 +406,9 @@ hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
   p.Tk = a.Tk;
   p.nqb = (a.Tq + kBM - 1) / kBM;
   p.total_wg = p.nqb * a.B * a.H;
-  p.scale_log2 = a.scale * kLog2e;
+  // A zero scale would make every score 0; a tiny positive factor gives the same softmax.
+  p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   void* args[] = {&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, OUT_F32>),
                          dim3(p.total_wg), dim3(kThreads), args, 0, stream);

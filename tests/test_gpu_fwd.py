@@ -141,10 +141,10 @@ def test_constant_values_give_that_constant(gpu):
     q, k, _ = si.make_inputs(wl, seed=10, threads=2)
     v = np.full_like(k, si.rne_bf16_bits(np.array([0.375], np.float32))[0])
     res = run_fwd(gpu, q, k, v, True, wl.scale)
-    # P is rounded to bf16 before the P V contraction while the denominator sums the fp32 p, so
-    # O = c * sum(bf16(p)) / sum(p): within half a bf16 ulp (2^-9 relative) of c, plus fp32 noise.
+    # O is normalised by the sum of the same bf16-rounded p the P V contraction used, so equal
+    # value rows come back up to fp32 summation-order noise.
     err = np.abs(res["o32"].cpu().numpy() - 0.375)
-    assert np.max(err) <= 0.375 * 2.0 ** -9 + 1e-6
+    assert np.max(err) <= 0.375 * 2e-5
     assert np.all(err[:, :, 0] == 0.0)   # row 0 sees one key: p = 1 exactly
 
 
