@@ -90,6 +90,41 @@ __global__ __launch_bounds__(256) void k_valu(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// MFMA / VALU co-execution: 512-thread workgroups (two waves per SIMD); waves 0-3 run an MFMA
+// loop (4 accumulator chains), waves 4-7 an fp32 FMA + v_exp loop.  mode 0 runs both, 1 only
+// the MFMA waves, 2 only the VALU waves.
+__global__ __launch_bounds__(512) void k_coexec(float* out, int mfma_iters, int valu_iters,
+                                                int mode) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  float s = 0.f;
+  if (w < 4) {
+    if (mode == 2) return;
+    bf16x8_t a, b;
+    for (int j = 0; j < 8; ++j) {
+      a[j] = (__bf16)(0.001f * (l + j));
+      b[j] = (__bf16)(0.002f * (l - j));
+    }
+    f32x16_t c[4];
+    for (int i = 0; i < 4; ++i) c[i] = f32x16_t{};
+    for (int it = 0; it < mfma_iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+    }
+    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 16; ++j) s += c[i][j];
+  } else {
+    if (mode == 1) return;
+    float x[8];
+    for (int i = 0; i < 8; ++i) x[i] = 0.5f + 0.01f * i + 1e-6f * l;
+    for (int it = 0; it < valu_iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(-__builtin_fmaf(x[i], 0.999f, 0.001f));
+    }
+    for (int i = 0; i < 8; ++i) s += x[i];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // LDS: 64 KB per workgroup; lane l of wave w reads 16 bytes at ((w*64 + l + 64*k) * 16) mod 64 KB.
 __global__ __launch_bounds__(256) void k_lds_b128(uint32_t* out, int iters) {
   __shared__ __attribute__((aligned(16))) uint32_t sm[16384];
@@ -184,6 +219,11 @@ int calib_valu(float* out, int blocks, int iters, int op, void* s) {
     case 3: hipLaunchKernelGGL(k_valu<3>, dim3(blocks), dim3(256), 0, st, out, iters); break;
     default: hipLaunchKernelGGL(k_valu<4>, dim3(blocks), dim3(256), 0, st, out, iters); break;
   }
+  return (int)hipGetLastError();
+}
+int calib_coexec(float* out, int blocks, int mfma_iters, int valu_iters, int mode, void* s) {
+  hipLaunchKernelGGL(k_coexec, dim3(blocks), dim3(512), 0, (hipStream_t)s, out, mfma_iters,
+                     valu_iters, mode);
   return (int)hipGetLastError();
 }
 int calib_lds_b128(uint32_t* out, int blocks, int iters, void* s) {

@@ -62,6 +62,15 @@ def main():
         insts = blocks * 4 * iters * 16
         res[f"valu_{name}_wave_insts_per_clk_per_cu"] = insts / t / cus / 2.4e9
 
+    # MFMA waves and VALU waves sharing SIMDs: time each alone and together
+    times = {}
+    for mode, name in ((1, "mfma_only"), (2, "valu_only"), (0, "both")):
+        times[name] = _time(lambda: lib.calib_coexec(ctypes.c_void_p(out.data_ptr()), cus, 8000,
+                                                     16000, mode, st))
+        res[f"coexec_ms_{name}"] = times[name] * 1e3
+    res["coexec_overlap"] = ((times["mfma_only"] + times["valu_only"] - times["both"]) /
+                             min(times["mfma_only"], times["valu_only"]))
+
     outu = out.view(torch.int32)
     blocks_l = cus * 2
     iters = 20000

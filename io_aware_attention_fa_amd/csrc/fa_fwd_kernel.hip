@@ -14,25 +14,26 @@
 //     and 16 of the tile's keys per 32-key block, so the row max and row sum are in-lane
 //     reductions plus one exchange with lane ^ 32 (v_permlane32_swap).
 //   * The P V contraction is also computed transposed, O^T += V^T P^T: P^T comes straight from
-//     the score registers (rounded to bf16) as the B operand, V^T is the A operand read from
-//     LDS.  V is transposed while it is staged into LDS, with its key columns permuted so that
-//     the 8 keys a lane holds in P are 8 adjacent LDS columns.
+//     the score registers (rounded to bf16) as the B operand; the V^T A operand is read from
+//     row-major V in LDS with the gfx950 transposing LDS read (two ds_read_b64_tr_b16 per
+//     MFMA), whose lane layout lands on exactly the keys each lane holds in P.
 //   * Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the four SIMDs pairwise and run
 //     the same program half a step apart.  Each step is a matrix section (this tile's S^T and
 //     the previous tile's O^T, 32 MFMAs, issued at raised priority) followed by a vector section
 //     (online softmax of this tile and staging of a later K/V tile into LDS), each closed by a
 //     workgroup barrier; group B starts one section late, so on every SIMD one wave feeds the
 //     matrix core while the other runs the exp/max/sum work.
-//   * K/V tiles live in a 4-deep ring of LDS stages (4 x 35 KB): tile t+3 is loaded into one of
-//     two register sets in matrix section t and written to LDS in vector section t+1.
+//   * K/V tiles live in a 4-deep ring of LDS stages (4 x 35 KB).  Three register sets carry
+//     tiles from HBM/L2 to LDS: tile t+4 is loaded in matrix section t and written to LDS in
+//     vector section t+2, so a global load has four sections to land.
 //   * Online softmax in log2 units with scale * log2(e) folded into one fused multiply-add per
 //     score; the row max is taken on the raw scores.  P is rounded to bf16 for the O^T MFMA and
 //     O is normalised by the sum of those rounded values (a v_dot2 against (1, 1) per pair), so
 //     O is an exact convex combination of the V rows the MFMA used; the LSE takes the sum of
-//     the fp32 p.  The rescale of the accumulator by
-//     exp(m_old - m_new) is skipped (one wave-uniform branch) unless some row's max has grown by
-//     more than 2^8 since the last rescale: stale maxima only scale p, l and acc by the same
-//     factor (at most 256), so O = acc / l and LSE = m + log l are unchanged.
+//     the fp32 p.  The rescale of the accumulator by exp(m_old - m_new) is skipped (one
+//     wave-uniform branch) unless some row's max has grown by more than 2^8 since the last
+//     rescale: stale maxima only scale p, l and acc by the same factor (at most 256), so
+//     O = acc / l and LSE = m + log l are unchanged.
 //   * Buffer loads with a per-head range return zeros past the end of Q/K/V, so ragged tails
 //     need only the -inf score mask (page "Chapter 10 Writing and Benchmarking Custom
 //     Kernels", section 10.3.1, "What You Actually Decide in Practice": the final partial tile).
@@ -56,6 +57,7 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;     // LDS ring depth
+constexpr int kSets = 3;       // register sets staging tiles into LDS
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 struct FwdParams {
@@ -69,69 +71,62 @@ struct FwdParams {
   uint32_t q_sign;    // 0x80008000 when scale < 0 (Q is negated instead), else 0
 };
 
-// Column of the V^T tile that holds key c (an involution): inside each group of 16 keys the
-// 4-key blocks 1 and 2 swap places.  This makes LDS columns [16s + 8g, 16s + 8g + 8) hold
-// exactly the keys that lane group g holds in registers 8*(s%2) .. 8*(s%2)+7 of the score
-// block s/2 (MFMA output rows 8*(i/4) + 4g + (i%4)).
-__host__ __device__ constexpr int vt_col(int c) {
-  const int blk = (c >> 2) & 3;
-  const int nb = blk == 1 ? 2 : (blk == 2 ? 1 : blk);
-  return (c & ~15) | (nb << 2) | (c & 3);
-}
-
 template <int D>
 struct Tile {
   static constexpr int KSTR = D + 8;           // bf16 per K row in LDS (16-byte pad)
-  static constexpr int VSTR = kBN + 8;         // bf16 per V^T row in LDS (16-byte pad)
+  static constexpr int VSTR = D + 16;          // bf16 per V row in LDS (32-byte pad)
   static constexpr int KELEMS = kBN * KSTR;
-  static constexpr int VELEMS = D * VSTR;
+  static constexpr int VELEMS = kBN * VSTR;
   static constexpr int STAGE = KELEMS + VELEMS;
-  static constexpr int KCHUNKS = kBN * D / 8 / kThreads;   // 16-byte K chunks per thread
-  static constexpr int VPAIRS = 32 * (D / 8);              // (2-key group, 8-d chunk) pairs
-  static_assert(KCHUNKS >= 1 && VPAIRS <= kThreads, "staging layout");
+  static constexpr int CHUNKS = kBN * D / 8 / kThreads;   // 16-byte chunks per thread, K and V
+  static_assert(CHUNKS >= 1, "staging layout");
 };
 
-// Global -> registers: this thread's share of the K/V tile starting at key j0.
+// One register set staging a K/V tile on its way to LDS.
+template <int D>
+struct Staged {
+  u32x4_t k[Tile<D>::CHUNKS];
+  u32x4_t v[Tile<D>::CHUNKS];
+};
+
+// Global -> registers: this thread's 16-byte chunks of the K/V tile starting at key j0.
+// Loads past the end of the tensor return zeros (buffer range); callers issue them anyway and
+// never store them, so every step issues the same number of loads and the compiler waits for
+// exactly the oldest register set instead of draining every load in flight.
 template <int D>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int j0, int tid, u32x4_t (&kr)[Tile<D>::KCHUNKS],
-                                          u32x4_t (&vr)[2]) {
+                                          int j0, int tid, Staged<D>& r) {
 #pragma unroll
-  for (int it = 0; it < Tile<D>::KCHUNKS; ++it) {
+  for (int it = 0; it < Tile<D>::CHUNKS; ++it) {
     const int c = tid + kThreads * it;
     const int row = c / (D / 8), col8 = c % (D / 8);
-    kr[it] = buf_load16(rk, (uint32_t)((j0 + row) * D + col8 * 8) * 2u);
-  }
-  if (tid < Tile<D>::VPAIRS) {
-    const int kg = tid & 31, dc = tid >> 5;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      vr[r] = buf_load16(rv, (uint32_t)((j0 + 2 * kg + r) * D + dc * 8) * 2u);
+    const uint32_t off = (uint32_t)((j0 + row) * D + col8 * 8) * 2u;
+    r.k[it] = buf_load16(rk, off);
+    r.v[it] = buf_load16(rv, off);
   }
 }
 
-// Registers -> LDS stage: K row-major, V transposed with permuted key columns.
+// Registers -> LDS stage: K and V both row-major with padded rows.
 template <int D>
-__device__ __forceinline__ void store_tile(uint16_t* stage, int tid,
-                                           const u32x4_t (&kr)[Tile<D>::KCHUNKS],
-                                           const u32x4_t (&vr)[2]) {
+__device__ __forceinline__ void store_tile(uint16_t* stage, int tid, const Staged<D>& r) {
   using T = Tile<D>;
 #pragma unroll
-  for (int it = 0; it < T::KCHUNKS; ++it) {
+  for (int it = 0; it < T::CHUNKS; ++it) {
     const int c = tid + kThreads * it;
     const int row = c / (D / 8), col8 = c % (D / 8);
-    *reinterpret_cast<u32x4_t*>(stage + row * T::KSTR + col8 * 8) = kr[it];
+    *reinterpret_cast<u32x4_t*>(stage + row * T::KSTR + col8 * 8) = r.k[it];
+    *reinterpret_cast<u32x4_t*>(stage + T::KELEMS + row * T::VSTR + col8 * 8) = r.v[it];
   }
-  if (tid < T::VPAIRS) {
-    const int kg = tid & 31, dc = tid >> 5;
-    uint16_t* vt = stage + T::KELEMS + vt_col(2 * kg);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      *reinterpret_cast<uint32_t*>(vt + (dc * 8 + dd) * T::VSTR) =
-          __builtin_amdgcn_perm(vr[1][dd >> 1], vr[0][dd >> 1], sel);   // keys 2kg, 2kg+1
-    }
-  }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j receives,
+// for t = 0..3, the 16-bit element j % 4 of the 8 bytes addressed by lane 4t + j / 4.
+__device__ __forceinline__ u32x2_t lds_read_tr(const uint16_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t* lds_ptr_t;
+  const s16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // A lane's value and the value of lane l ^ 32.  With both operands holding v,
@@ -166,6 +161,7 @@ void fa_fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
+  // waves w and w + 4 share a SIMD: one from each group
   const bool group_b = wave >= 4;
 
   // ---- workgroup -> (batch*head, query block) ----
@@ -205,6 +201,16 @@ void fa_fwd_kernel(FwdParams p) {
 
   auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
 
+  // Per-lane LDS offsets (elements) of the MFMA A operands inside a stage.
+  //  K (S^T = K Q^T): row 32*kb + r32, d 16*s + 8g  ->  k_off + 32*kb*KSTR + 16*s.
+  //  V^T (O^T += V^T P^T) via the transposing read: lane l of 16-lane group (g, dh) addresses
+  //  key 16*ks + 8*h + 4*g + (l % 16) / 4, d 32*db + 16*dh + 4*(l % 4), and receives V^T row
+  //  d = 32*db + (l % 32), keys 16*ks + 8*h + 4*g + 0..3 (the keys it holds in P registers
+  //  8*(ks%2) + 4*h .. +3 of score block ks/2).
+  const int k_off = r32 * T::KSTR + 8 * g;
+  const int v_off = T::KELEMS + (4 * g + ((lane & 15) >> 2)) * T::VSTR +
+                    16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
   float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
   float l_run = 0.f;         // this lane's partial running sum of p (fp32): the LSE
   float l16_run = 0.f;       // this lane's partial running sum of bf16(p): normalises O
@@ -214,46 +220,44 @@ void fa_fwd_kernel(FwdParams p) {
   f32x16_t sacc[2];
   bf16x8_t pb[4];
 
-  // ---- prologue: tiles 0 and 1 into stages 0 and 1 ----
-  // Two register sets stage K/V tiles on their way to LDS: tile x uses set x % 2.  Tile t+3 is
-  // loaded in matrix section t and written to LDS in vector section t+1, so a global load has
-  // two sections to land.
-  u32x4_t kr0[T::KCHUNKS], vr0[2], kr1[T::KCHUNKS], vr1[2];
-  load_tile<D>(rk, rv, 0, tid, kr0, vr0);
-  store_tile<D>(lds, tid, kr0, vr0);
-  if (ntiles > 1) {
-    load_tile<D>(rk, rv, kBN, tid, kr1, vr1);
-    store_tile<D>(lds + T::STAGE, tid, kr1, vr1);
-  }
-  if (ntiles > 2) load_tile<D>(rk, rv, 2 * kBN, tid, kr0, vr0);
+  // ---- prologue: tiles 0 and 1 into LDS stages 0 and 1, tiles 2 and 3 into register sets ----
+  Staged<D> rs0, rs1, rs2;   // tile x lives in set x % 3
+  load_tile<D>(rk, rv, 0, tid, rs0);
+  load_tile<D>(rk, rv, kBN, tid, rs1);
+  store_tile<D>(lds, tid, rs0);
+  store_tile<D>(lds + T::STAGE, tid, rs1);
+  load_tile<D>(rk, rv, 2 * kBN, tid, rs2);
+  load_tile<D>(rk, rv, 3 * kBN, tid, rs0);
   __syncthreads();
   if (group_b) __syncthreads();   // group B runs one section behind group A
 
-  auto step = [&](const int t, auto parity) {
-    constexpr int P = decltype(parity)::value;   // == t % 2
-    auto& kr_store = P ? kr1 : kr0;   // tile t+2
-    auto& vr_store = P ? vr1 : vr0;
-    auto& kr_load = P ? kr0 : kr1;    // tile t+3
-    auto& vr_load = P ? vr0 : vr1;
+  auto step = [&](const int t, auto phase) {
+    constexpr int P = decltype(phase)::value;   // == t % 3
+    Staged<D>& rs_load = P == 0 ? rs1 : (P == 1 ? rs2 : rs0);    // tile t+4: set (t+1) % 3
+    Staged<D>& rs_store = P == 0 ? rs2 : (P == 1 ? rs0 : rs1);   // tile t+2: set (t+2) % 3
+
     // ================= matrix section =================
     __builtin_amdgcn_s_setprio(1);
-    if (t + 3 < ntiles) load_tile<D>(rk, rv, (t + 3) * kBN, tid, kr_load, vr_load);
+    load_tile<D>(rk, rv, (t + 4) * kBN, tid, rs_load);
     {
       // Operands stream through a ring of kRing LDS reads issued ahead of the MFMAs that use
       // them: first the 2*NS K operands of S^T = K Q^T, then the 4*ND V^T operands of
       // O^T += V^T P^T.  The three cases (both products, S^T only on the first tile, O^T only
       // after the last) are separate compile-time instances so every ring index is static.
       constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
-      const uint16_t* ks = lds + (t % kStages) * T::STAGE + r32 * T::KSTR + 8 * g;
-      const uint16_t* vt = lds + ((t + kStages - 1) % kStages) * T::STAGE + T::KELEMS +
-                           r32 * T::VSTR + 8 * g;
+      const uint16_t* ks = lds + (t % kStages) * T::STAGE + k_off;
+      const uint16_t* vs = lds + ((t + kStages - 1) % kStages) * T::STAGE + v_off;
       // operand i < NK: K rows 32*(i%2) + r32, d 16*(i/2) + 8g; i >= NK: V^T rows
-      // 32*(j%ND) + r32, keys 16*(j/ND) + 8g with j = i - NK.
+      // 32*(j%ND) + (l%32), keys 16*(j/ND) + 8g.. with j = i - NK (two transposing reads).
       auto opnd = [&](int i) -> bf16x8_t {
         if (i < NK)
           return *reinterpret_cast<const bf16x8_t*>(ks + (32 * (i & 1)) * T::KSTR + 16 * (i >> 1));
         const int j = i - NK;
-        return *reinterpret_cast<const bf16x8_t*>(vt + (32 * (j % ND)) * T::VSTR + 16 * (j / ND));
+        const uint16_t* base = vs + (16 * (j / ND)) * T::VSTR + 32 * (j % ND);
+        const u32x2_t lo = lds_read_tr(base);
+        const u32x2_t hi = lds_read_tr(base + 8 * T::VSTR);
+        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        return as_bf16x8(w);
       };
       auto section = [&](auto with_s, auto with_o) {
         constexpr int first = decltype(with_s)::value ? 0 : NK;
@@ -277,14 +281,22 @@ void fa_fwd_kernel(FwdParams p) {
             oacc[j % ND] = mfma_32x32x16(a, pb[j / ND], oacc[j % ND]);
           }
         }
-        // keep kRing LDS reads in flight: kRing reads, then (MFMA, read) pairs, then MFMAs
+        // keep the operand reads ahead of the MFMAs: reads for the first kRing operands, then
+        // (MFMA, reads) pairs, then the last MFMAs
         constexpr int n = last - first;
         constexpr int ahead = n < kRing ? n : kRing;
-        __builtin_amdgcn_sched_group_barrier(0x100, ahead, 0);
+        constexpr int nk_in = first == 0 ? (NK < ahead ? NK : ahead) : 0;
+        __builtin_amdgcn_sched_group_barrier(0x100, nk_in + 2 * (ahead - nk_in), 0);
+        constexpr int k_after = NK - first - ahead > 0 ? NK - first - ahead : 0;   // K reads
 #pragma unroll
-        for (int i = 0; i < n - ahead; ++i) {
+        for (int i = 0; i < k_after; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = k_after; i < n - ahead; ++i) {   // V^T operands: two transposing reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
       };
@@ -314,11 +326,14 @@ void fa_fwd_kernel(FwdParams p) {
               if (key > lim) sacc[kb][i] = -INFINITY;
             }
         }
-        float mt = fmaxf(sacc[0][0], sacc[0][1]);
+        // Every reduction below runs as four independent chains: one wave per SIMD does this
+        // work while the other issues MFMAs, so dependent-issue latency is not hidden by others.
+        float mx[4];
 #pragma unroll
-        for (int i = 2; i < 16; ++i) mt = fmaxf(mt, sacc[0][i]);
+        for (int c = 0; c < 4; ++c) mx[c] = fmaxf(sacc[0][c], sacc[0][c + 4]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
+        for (int i = 8; i < 32; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[i >> 4][i & 15]);
+        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = xhalf_max(mt) * p.scale_log2;
         // lazy rescale: only when some row's max outgrew the max in use by > 2^8
         if (__any(mt > m_run + kRescaleThreshold)) {
@@ -332,17 +347,18 @@ void fa_fwd_kernel(FwdParams p) {
             for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
           m_run = m_new;
         }
-        float psum = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
             sacc[kb][i] = e;
-            psum += e;
+            ps[i & 3] += e;
           }
-        l_run += psum;
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
+        float l16[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const f32x16_t& sb = sacc[ks >> 1];
@@ -353,22 +369,23 @@ void fa_fwd_kernel(FwdParams p) {
           pb[ks] = as_bf16x8(w);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            l16_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]),
-                                                      ones_bf16x2(), l16_run, false);
+            l16[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(), l16[e],
+                                                     false);
         }
+        l16_run += (l16[0] + l16[1]) + (l16[2] + l16[3]);
       }
-      if (t + 2 < ntiles)
-        store_tile<D>(lds + ((t + 2) % kStages) * T::STAGE, tid, kr_store, vr_store);
+      if (t + 2 < ntiles) store_tile<D>(lds + ((t + 2) % kStages) * T::STAGE, tid, rs_store);
     }
     __syncthreads();
   };
-  for (int t = 0; t <= ntiles; t += 2) {
+  for (int t = 0; t <= ntiles; t += kSets) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
   }
   if (!group_b) __syncthreads();   // match group B's extra barrier
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ----
+  // ---- epilogue: O = acc / l16, LSE = (m + log2 l) * ln 2 ----
   if (!wave_has_rows) return;
   const float l_tot = xhalf_sum(l_run);
   const float l16_tot = xhalf_sum(l16_run);
