@@ -23,9 +23,12 @@
 //     (online softmax of this tile and staging of a later K/V tile into LDS), each closed by a
 //     workgroup barrier; group B starts one section late, so on every SIMD one wave feeds the
 //     matrix core while the other runs the exp/max/sum work.
-//   * K/V tiles live in a 4-deep ring of LDS stages (4 x 35 KB).  Three register sets carry
-//     tiles from HBM/L2 to LDS: tile t+4 is loaded in matrix section t and written to LDS in
-//     vector section t+2, so a global load has four sections to land.
+//   * K/V tiles live in a 4-deep ring of LDS stages (4 x 32 KB at d = 128), filled by direct
+//     global-to-LDS loads (buffer_load ... lds): no registers, no LDS store instructions and no
+//     waits in the vector sections.  Tile t+2 is requested at the start of matrix section t and
+//     waited for at the end of matrix section t+1.  Each 64-lane load writes 1 KB of LDS
+//     contiguously, so rows cannot be padded; instead the 16-byte chunks of each row are
+//     XOR-swizzled so that the MFMA operand reads hit distinct LDS banks.
 //   * Online softmax in log2 units with scale * log2(e) folded into one fused multiply-add per
 //     score; the row max is taken on the raw scores.  P is rounded to bf16 for the O^T MFMA and
 //     O is normalised by the sum of those rounded values (a v_dot2 against (1, 1) per pair), so
@@ -57,8 +60,12 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;     // LDS ring depth
-constexpr int kSets = 3;       // register sets staging tiles into LDS
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8),
+// waiting on vector-memory operations only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 struct FwdParams {
   const uint16_t* q;
@@ -73,60 +80,64 @@ struct FwdParams {
 
 template <int D>
 struct Tile {
-  static constexpr int KSTR = D + 8;           // bf16 per K row in LDS (16-byte pad)
-  static constexpr int VSTR = D + 16;          // bf16 per V row in LDS (32-byte pad)
-  static constexpr int KELEMS = kBN * KSTR;
-  static constexpr int VELEMS = kBN * VSTR;
-  static constexpr int STAGE = KELEMS + VELEMS;
-  static constexpr int CHUNKS = kBN * D / 8 / kThreads;   // 16-byte chunks per thread, K and V
-  static_assert(CHUNKS >= 1, "staging layout");
-};
-
-// One register set staging a K/V tile on its way to LDS.
-template <int D>
-struct Staged {
-  u32x4_t k[Tile<D>::CHUNKS];
-  u32x4_t v[Tile<D>::CHUNKS];
-};
-
-// Global -> registers: this thread's 16-byte chunks of the K/V tile starting at key j0.
-// Loads past the end of the tensor return zeros (buffer range); callers issue them anyway and
-// never store them, so every step issues the same number of loads and the compiler waits for
-// exactly the oldest register set instead of draining every load in flight.
-template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int j0, int tid, Staged<D>& r) {
-#pragma unroll
-  for (int it = 0; it < Tile<D>::CHUNKS; ++it) {
-    const int c = tid + kThreads * it;
-    const int row = c / (D / 8), col8 = c % (D / 8);
-    const uint32_t off = (uint32_t)((j0 + row) * D + col8 * 8) * 2u;
-    r.k[it] = buf_load16(rk, off);
-    r.v[it] = buf_load16(rv, off);
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int TILE = kBN * D;               // bf16 per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;             // K then V
+  static constexpr int ROWS_PER_LOAD = 64 / CH;      // rows one 64-lane load (1 KB) covers
+  static constexpr int LOADS = kBN / ROWS_PER_LOAD;  // 1 KB loads per tile and tensor
+  static constexpr int LOADS_PER_WAVE = LOADS / kWaves;
+  static_assert(LOADS_PER_WAVE >= 1 && LOADS % kWaves == 0, "staging layout");
+  // Physical 16-byte chunk of logical chunk c in row r (an involution, so it also maps back).
+  // LDS serves 256 bytes per clock: one d = 128 row, or two d = 64 rows.  K is read 16 rows x
+  // one chunk per 16 lanes, so rows that share banks get distinct chunks.  V is read by the
+  // transposing load, 4 rows x 4 chunks per 32 lanes, so each row's 4-chunk group moves to its
+  // own 64-byte quarter of the banks.
+  static __device__ __forceinline__ int kchunk(int r, int c) {
+    return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
   }
+  static __device__ __forceinline__ int vchunk(int r, int c) {
+    return D == 128 ? c ^ (4 * (r & 3)) : c ^ (4 * ((r >> 1) & 1));
+  }
+};
+
+// Loads one wave issues per tile (K and V).
+template <int D>
+constexpr int kVmcntTile = vmcnt_imm(2 * Tile<D>::LOADS_PER_WAVE);
+
+// One buffer_load_dwordx4 ... lds: lane l reads 16 bytes at byte offset voff of the buffer
+// (zeros past its end) and writes them to LDS bytes [m0 + 16*l, m0 + 16*l + 16).  Written as
+// inline assembly so that the compiler neither tracks it (it would otherwise wait for the load
+// before any later LDS read it cannot prove disjoint) nor moves LDS accesses across it; the
+// kernel waits for these loads itself with s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t m0, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
 }
 
-// Registers -> LDS stage: K and V both row-major with padded rows.
-template <int D>
-__device__ __forceinline__ void store_tile(uint16_t* stage, int tid, const Staged<D>& r) {
-  using T = Tile<D>;
-#pragma unroll
-  for (int it = 0; it < T::CHUNKS; ++it) {
-    const int c = tid + kThreads * it;
-    const int row = c / (D / 8), col8 = c % (D / 8);
-    *reinterpret_cast<u32x4_t*>(stage + row * T::KSTR + col8 * 8) = r.k[it];
-    *reinterpret_cast<u32x4_t*>(stage + T::KELEMS + row * T::VSTR + col8 * 8) = r.v[it];
-  }
+// Buffer resource words for lds_dma16: base, stride 0, byte range, raw 32-bit dword format.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j receives,
 // for t = 0..3, the 16-bit element j % 4 of the 8 bytes addressed by lane 4t + j / 4.
-__device__ __forceinline__ u32x2_t lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4_t* lds_ptr_t;
-  const s16x4_t v =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p)));
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16-byte LDS read at a byte address.
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const bf16x8_t* lds_ptr_t;
+  return *(lds_ptr_t)(uintptr_t)addr;
 }
 
 // A lane's value and the value of lane l ^ 32.  With both operands holding v,
@@ -157,9 +168,15 @@ void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
   constexpr int NS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int ND = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * T::STAGE];
+  // LDS: the four K stages, then the four V stages.  Every access below is a per-lane base
+  // address (fixed for the whole kernel) plus a compile-time offset below 64 KB, which the
+  // LDS instructions take as an immediate.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  constexpr uint32_t kTileBytes = T::TILE * 2, kVRegion = kStages * kTileBytes;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
   // waves w and w + 4 share a SIMD: one from each group
   const bool group_b = wave >= 4;
@@ -178,8 +195,8 @@ void fa_fwd_kernel(FwdParams p) {
   const size_t qbase = (size_t)bh * (size_t)p.Tq * D;
   const size_t kbase = (size_t)bh * (size_t)p.Tk * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qbase, (uint32_t)p.Tq * D * 2u);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kbase, (uint32_t)p.Tk * D * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kbase, (uint32_t)p.Tk * D * 2u);
+  const u32x4_t rk = rsrc_words(p.k + kbase, (uint32_t)p.Tk * D * 2u);
+  const u32x4_t rv = rsrc_words(p.v + kbase, (uint32_t)p.Tk * D * 2u);
 
   // ---- this wave's 32 query rows; Q fragment kept in registers ----
   const int qw0 = i0 + wave * 32;
@@ -201,15 +218,34 @@ void fa_fwd_kernel(FwdParams p) {
 
   auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
 
-  // Per-lane LDS offsets (elements) of the MFMA A operands inside a stage.
-  //  K (S^T = K Q^T): row 32*kb + r32, d 16*s + 8g  ->  k_off + 32*kb*KSTR + 16*s.
-  //  V^T (O^T += V^T P^T) via the transposing read: lane l of 16-lane group (g, dh) addresses
-  //  key 16*ks + 8*h + 4*g + (l % 16) / 4, d 32*db + 16*dh + 4*(l % 4), and receives V^T row
-  //  d = 32*db + (l % 32), keys 16*ks + 8*h + 4*g + 0..3 (the keys it holds in P registers
-  //  8*(ks%2) + 4*h .. +3 of score block ks/2).
-  const int k_off = r32 * T::KSTR + 8 * g;
-  const int v_off = T::KELEMS + (4 * g + ((lane & 15) >> 2)) * T::VSTR +
-                    16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Per-lane LDS byte addresses of the MFMA A operands in stage 0; stage x adds x * kTileBytes.
+  //  K (S^T = K Q^T), k-step s, key block kb: row 32*kb + r32, logical chunk 2*s + g.  The
+  //  swizzle is an XOR on the chunk index and depends on the row only through r32, so the
+  //  address is k_base ^ (32*s), plus 32*kb*D*2 bytes.
+  //  V^T (O^T += V^T P^T) via the transposing read, 32-row block db of O^T, k-step ks, half hf:
+  //  lane l of 16-lane group (g, dh) addresses key 16*ks + 8*hf + 4*g + (l % 16) / 4,
+  //  d = 32*db + 16*dh + 4*(l % 4), and receives V^T row d = 32*db + (l % 32), keys
+  //  16*ks + 8*hf + 4*g + 0..3 (the keys it holds in P registers 8*(ks%2) + 4*hf .. +3 of score
+  //  block ks/2).  The swizzle depends on the key only through (l % 16) / 4, so the address is
+  //  v_base ^ (64*db), plus (16*ks + 8*hf)*D*2 bytes.
+  const uint32_t k_base = lds0 + 2 * (r32 * D + 8 * T::kchunk(r32, g));
+  uint32_t v_base;
+  {
+    const int x = (lane & 15) >> 2, dh = (lane >> 4) & 1, r = 4 * g + x;
+    v_base = lds0 + kVRegion +
+             2 * (r * D + 8 * T::vchunk(r, 2 * dh + ((lane & 3) >> 1)) + 4 * (lane & 1));
+  }
+  // This wave's share of a tile load: LOADS_PER_WAVE 1 KB pieces of K and of V.  Lane l of
+  // piece n fills tile row n * ROWS_PER_LOAD + l / CH, physical chunk l % CH, so it reads the
+  // logical chunk that the swizzle maps there.
+  uint32_t dk[T::LOADS_PER_WAVE], dv[T::LOADS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+    const int r = (wave * T::LOADS_PER_WAVE + i) * T::ROWS_PER_LOAD + lane / T::CH;
+    const int pc = lane % T::CH;
+    dk[i] = 2u * (uint32_t)(r * D + 8 * T::kchunk(r, pc));
+    dv[i] = 2u * (uint32_t)(r * D + 8 * T::vchunk(r, pc));
+  }
 
   float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
   float l_run = 0.f;         // this lane's partial running sum of p (fp32): the LSE
@@ -220,42 +256,57 @@ void fa_fwd_kernel(FwdParams p) {
   f32x16_t sacc[2];
   bf16x8_t pb[4];
 
-  // ---- prologue: tiles 0 and 1 into LDS stages 0 and 1, tiles 2 and 3 into register sets ----
-  Staged<D> rs0, rs1, rs2;   // tile x lives in set x % 3
-  load_tile<D>(rk, rv, 0, tid, rs0);
-  load_tile<D>(rk, rv, kBN, tid, rs1);
-  store_tile<D>(lds, tid, rs0);
-  store_tile<D>(lds + T::STAGE, tid, rs1);
-  load_tile<D>(rk, rv, 2 * kBN, tid, rs2);
-  load_tile<D>(rk, rv, 3 * kBN, tid, rs0);
+  // Tile x occupies stage x % 4.  Tile x + 2 is requested at the start of matrix section x;
+  // each wave waits for its own part of tile x + 1 at the end of matrix section x (one more
+  // tile may still be in flight), and the barrier that follows publishes it to all waves.
+  auto request = [&](int x) {
+    if (x < ntiles) {
+      const uint32_t so = (uint32_t)(x % kStages) * kTileBytes;
+      const uint32_t g0 = (uint32_t)x * (kBN * D * 2);
+#pragma unroll
+      for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+        const uint32_t piece = (uint32_t)(wave * T::LOADS_PER_WAVE + i) * 1024u;
+        lds_dma16(rk, lds0 + so + piece, g0 + dk[i]);
+        lds_dma16(rv, lds0 + kVRegion + so + piece, g0 + dv[i]);
+      }
+    }
+  };
+  auto wait_next = [&](int x) {   // tile x + 1 has landed (this wave's part)
+    if (x + 2 < ntiles)
+      __builtin_amdgcn_s_waitcnt(kVmcntTile<D>);
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  };
+
+  // ---- prologue: Q and tiles 0 and 1 loaded and published ----
+  // (a full wait: it also settles the Q loads, which the compiler would otherwise wait for at
+  // their first use, behind the next tile's loads)
+  request(0);
+  request(1);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   if (group_b) __syncthreads();   // group B runs one section behind group A
 
-  auto step = [&](const int t, auto phase) {
-    constexpr int P = decltype(phase)::value;   // == t % 3
-    Staged<D>& rs_load = P == 0 ? rs1 : (P == 1 ? rs2 : rs0);    // tile t+4: set (t+1) % 3
-    Staged<D>& rs_store = P == 0 ? rs2 : (P == 1 ? rs0 : rs1);   // tile t+2: set (t+2) % 3
-
+  auto step = [&](const int t, auto first_step) {
     // ================= matrix section =================
     __builtin_amdgcn_s_setprio(1);
-    load_tile<D>(rk, rv, (t + 4) * kBN, tid, rs_load);
+    request(t + 2);
     {
       // Operands stream through a ring of kRing LDS reads issued ahead of the MFMAs that use
       // them: first the 2*NS K operands of S^T = K Q^T, then the 4*ND V^T operands of
-      // O^T += V^T P^T.  The three cases (both products, S^T only on the first tile, O^T only
-      // after the last) are separate compile-time instances so every ring index is static.
+      // O^T += V^T P^T.  The two cases (S^T only on the first tile, both products after it)
+      // are separate compile-time instances so every ring index is static.
       constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
-      const uint16_t* ks = lds + (t % kStages) * T::STAGE + k_off;
-      const uint16_t* vs = lds + ((t + kStages - 1) % kStages) * T::STAGE + v_off;
-      // operand i < NK: K rows 32*(i%2) + r32, d 16*(i/2) + 8g; i >= NK: V^T rows
-      // 32*(j%ND) + (l%32), keys 16*(j/ND) + 8g.. with j = i - NK (two transposing reads).
+      const uint32_t ks = k_base + (uint32_t)(t % kStages) * kTileBytes;              // tile t
+      const uint32_t vs = v_base + (uint32_t)((t + kStages - 1) % kStages) * kTileBytes;  // t - 1
+      // operand i < NK: K rows 32*(i%2) + r32, k-step i/2; i >= NK: V^T block db = j%ND, k-step
+      // ks = j/ND with j = i - NK (two transposing reads).
       auto opnd = [&](int i) -> bf16x8_t {
-        if (i < NK)
-          return *reinterpret_cast<const bf16x8_t*>(ks + (32 * (i & 1)) * T::KSTR + 16 * (i >> 1));
+        if (i < NK) return lds_read16((ks ^ (32u * (i >> 1))) + 2 * 32 * (i & 1) * D);
         const int j = i - NK;
-        const uint16_t* base = vs + (16 * (j / ND)) * T::VSTR + 32 * (j % ND);
+        const uint32_t base = (vs ^ (64u * (j % ND))) + 2 * 16 * (j / ND) * D;
         const u32x2_t lo = lds_read_tr(base);
-        const u32x2_t hi = lds_read_tr(base + 8 * T::VSTR);
+        const u32x2_t hi = lds_read_tr(base + 2 * 8 * D);
         const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
         return as_bf16x8(w);
       };
@@ -300,89 +351,88 @@ void fa_fwd_kernel(FwdParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
       };
-      const bool do_s = t < ntiles && active(t);
-      const bool do_o = t >= 1 && active(t - 1);
+      // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
+      // that has the previous tile's P^T to apply runs both products; at the step after its last
+      // tile the S^T product is wasted (and ignored), which keeps a single code path for the
+      // accumulators.
       using yes = std::true_type;
       using no = std::false_type;
-      if (do_s && do_o) section(yes{}, yes{});
-      else if (do_s) section(yes{}, no{});
-      else if (do_o) section(no{}, yes{});
+      if (decltype(first_step)::value) {
+        if (active(0)) section(yes{}, no{});
+      } else {
+        if (active(t - 1)) section(yes{}, yes{});
+      }
     }
+    wait_next(t);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
 
     // ================= vector section =================
-    if (t < ntiles) {
-      if (active(t)) {
-        const int j0 = t * kBN;
-        const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
-        if (need_mask) {
-          const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (key > lim) sacc[kb][i] = -INFINITY;
-            }
-        }
-        // Every reduction below runs as four independent chains: one wave per SIMD does this
-        // work while the other issues MFMAs, so dependent-issue latency is not hidden by others.
-        float mx[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mx[c] = fmaxf(sacc[0][c], sacc[0][c + 4]);
-#pragma unroll
-        for (int i = 8; i < 32; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[i >> 4][i & 15]);
-        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-        mt = xhalf_max(mt) * p.scale_log2;
-        // lazy rescale: only when some row's max outgrew the max in use by > 2^8
-        if (__any(mt > m_run + kRescaleThreshold)) {
-          const float m_new = fmaxf(m_run, mt);
-          const float corr = fast_exp2(m_run - m_new);
-          l_run *= corr;
-          l16_run *= corr;
-#pragma unroll
-          for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-          m_run = m_new;
-        }
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < ntiles && active(t)) {
+      const int j0 = t * kBN;
+      const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
-            sacc[kb][i] = e;
-            ps[i & 3] += e;
+            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > lim) sacc[kb][i] = -INFINITY;
           }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
-        float l16[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const f32x16_t& sb = sacc[ks >> 1];
-          const int b0 = (ks & 1) * 8;
-          const u32x2_t lo = pack_bf16x4(sb[b0], sb[b0 + 1], sb[b0 + 2], sb[b0 + 3]);
-          const u32x2_t hi = pack_bf16x4(sb[b0 + 4], sb[b0 + 5], sb[b0 + 6], sb[b0 + 7]);
-          u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-          pb[ks] = as_bf16x8(w);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            l16[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(), l16[e],
-                                                     false);
-        }
-        l16_run += (l16[0] + l16[1]) + (l16[2] + l16[3]);
       }
-      if (t + 2 < ntiles) store_tile<D>(lds + ((t + 2) % kStages) * T::STAGE, tid, rs_store);
+      // Every reduction below runs as four independent chains: one wave per SIMD does this
+      // work while the other issues MFMAs, so dependent-issue latency is not hidden by others.
+      float mx[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx[c] = fmaxf(sacc[0][c], sacc[0][c + 4]);
+#pragma unroll
+      for (int i = 8; i < 32; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[i >> 4][i & 15]);
+      float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      mt = xhalf_max(mt) * p.scale_log2;
+      // lazy rescale: only when some row's max outgrew the max in use by > 2^8
+      if (__any(mt > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float corr = fast_exp2(m_run - m_new);
+        l_run *= corr;
+        l16_run *= corr;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+        m_run = m_new;
+      }
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
+          sacc[kb][i] = e;
+          ps[i & 3] += e;
+        }
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
+      float l16[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x16_t& sb = sacc[ks >> 1];
+        const int b0 = (ks & 1) * 8;
+        const u32x2_t lo = pack_bf16x4(sb[b0], sb[b0 + 1], sb[b0 + 2], sb[b0 + 3]);
+        const u32x2_t hi = pack_bf16x4(sb[b0 + 4], sb[b0 + 5], sb[b0 + 6], sb[b0 + 7]);
+        u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        pb[ks] = as_bf16x8(w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          l16[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(), l16[e],
+                                                   false);
+      }
+      l16_run += (l16[0] + l16[1]) + (l16[2] + l16[3]);
     }
     __syncthreads();
   };
-  for (int t = 0; t <= ntiles; t += kSets) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 <= ntiles) step(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 <= ntiles) step(t + 2, std::integral_constant<int, 2>{});
-  }
+  step(0, std::true_type{});
+  for (int t = 1; t <= ntiles; ++t) step(t, std::false_type{});
   if (!group_b) __syncthreads();   // match group B's extra barrier
 
   // ---- epilogue: O = acc / l16, LSE = (m + log2 l) * ln 2 ----
