@@ -40,24 +40,30 @@ def upload(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def traffic_from_profiles(kernel_tag):
+def traffic_from_profiles(name):
     """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary, if any.
 
-    The summary file (profiles/<kernel_tag>_traffic.json) holds FETCH_SIZE / WRITE_SIZE per
-    dispatch already scaled by the copy-kernel calibration factor, and the hash of the kernel
-    source it was taken on; a stale summary (source changed since) gives null.
+    The summary (profiles/traffic__<name>.txt) holds FETCH_SIZE / WRITE_SIZE per dispatch
+    already scaled by the copy-kernel calibration factors, with the sha256 of the kernel sources
+    it was taken on; if those sources have changed since, the figure is stale and this gives None.
     """
-    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.json")
+    import hashlib
+    path = os.path.join(PROFILE_DIR, f"traffic__{name}.txt")
     if not os.path.exists(path):
         return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.partition(":")
+        if sep and key in ("sources", "sources_sha256", "hbm_bytes_per_launch"):
+            fields[key] = val.strip()
     try:
-        rec = json.load(open(path))
-        import hashlib
-        src = os.path.join(ROOT, rec["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        h = hashlib.sha256()
+        for src in fields["sources"].split():
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != fields["sources_sha256"]:
             return None
-        return float(rec["hbm_bytes_per_launch"])
-    except Exception:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
         return None
 
 
@@ -196,7 +202,7 @@ def main():
         out.update(value=tflops, unit="TFLOP/s")
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                            "frac": tflops / peak,
-                           "traffic": traffic_from_profiles("fa_fwd_kernel_d128_causal")}
+                           "traffic": traffic_from_profiles(f"fa_fwd_kernel__{PREFILL}")}
         config.update(prefill={"B": wp.B, "h": wp.h, "T": wp.Tq, "d_head": wp.d, "causal": True,
                                "avg_ms": p_ms, "min_ms": min(pt), "median_ms": sorted(pt)[K // 2],
                                "alg_bytes": cm.attention_io_bytes(wp.B, wp.h, wp.Tq, wp.Tk, wp.d),
@@ -213,7 +219,8 @@ def main():
                "unit": "GB/s",
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak_gbs, "unit": "GB/s",
                             "frac": gbs / peak_gbs,
-                            "traffic": traffic_from_profiles("fa_decode_split_kernel_d128")},
+                            "traffic": traffic_from_profiles(
+                                f"fa_decode_split_kernel__{DECODE}")},
                "avg_ms": d_ms, "min_ms": min(dt), "median_ms": sorted(dt)[K // 2],
                "config": {"B": wd.B, "h": wd.h, "Tk": wd.Tk, "d_head": wd.d,
                           "num_splits": wd.num_splits}}
