@@ -73,7 +73,9 @@ struct FwdParams {
   const uint16_t* v;
   void* o;
   float* lse;
-  int Tq, Tk, nqb, total_wg;
+  int Tq, Tk, nqb;
+  int BH, npairs;   // heads (batch * heads) and query-block pairs per head
+  int groups;       // workgroup groups (one per XCD); group x takes heads x, x + groups, ...
   float scale_log2;   // |scale| * log2(e), > 0
   uint32_t q_sign;    // 0x80008000 when scale < 0 (Q is negated instead), else 0
 };
@@ -181,43 +183,6 @@ void fa_fwd_kernel(FwdParams p) {
   // waves w and w + 4 share a SIMD: one from each group
   const bool group_b = wave >= 4;
 
-  // ---- workgroup -> (batch*head, query block) ----
-  const int n = blockIdx.x;
-  const int per = p.total_wg >> 3, rem = p.total_wg & 7, xcd = n & 7, loc = n >> 3;
-  const int logical =
-      xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-  const int bh = logical / p.nqb;
-  const int qr = logical - bh * p.nqb;
-  const int qb = CAUSAL ? p.nqb - 1 - qr : qr;
-  const int i0 = qb * kBM;
-  const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
-
-  const size_t qbase = (size_t)bh * (size_t)p.Tq * D;
-  const size_t kbase = (size_t)bh * (size_t)p.Tk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qbase, (uint32_t)p.Tq * D * 2u);
-  const u32x4_t rk = rsrc_words(p.k + kbase, (uint32_t)p.Tk * D * 2u);
-  const u32x4_t rv = rsrc_words(p.v + kbase, (uint32_t)p.Tk * D * 2u);
-
-  // ---- this wave's 32 query rows; Q fragment kept in registers ----
-  const int qw0 = i0 + wave * 32;
-  const int qrow = qw0 + r32;
-  const int qw_last = min(qw0 + 31, p.Tq - 1);
-  const bool wave_has_rows = qw0 < p.Tq;
-  bf16x8_t qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
-    w ^= p.q_sign;
-    qf[s] = as_bf16x8(w);
-  }
-
-  // keys the workgroup needs: all, or (causal) up to the block's last row
-  int kend = p.Tk;
-  if (CAUSAL) kend = min(p.Tk, min(i0 + kBM, p.Tq) + off);
-  const int ntiles = (kend + kBN - 1) / kBN;
-
-  auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
-
   // Per-lane LDS byte addresses of the MFMA A operands in stage 0; stage x adds x * kTileBytes.
   //  K (S^T = K Q^T), k-step s, key block kb: row 32*kb + r32, logical chunk 2*s + g.  The
   //  swizzle is an XOR on the chunk index and depends on the row only through r32, so the
@@ -247,9 +212,58 @@ void fa_fwd_kernel(FwdParams p) {
     dv[i] = 2u * (uint32_t)(r * D + 8 * T::vchunk(r, pc));
   }
 
+  // ---- static schedule ----
+  // The grid is at most one workgroup per CU.  Workgroup n belongs to group x = n % groups
+  // (the XCD it is dispatched to) and takes heads x, x + groups, ... of that group; the group's
+  // (head, block pair) list is dealt round-robin over its workgroups, so the workgroups of one
+  // XCD work on a few heads at a time and share their K/V in that XCD's L2.  A pair holds query
+  // blocks nqb-1-j and j, whose causal costs add up to the same total for every j.
+  const int n = blockIdx.x, X = p.groups;
+  const int x = __builtin_amdgcn_readfirstlane(n % X), c = __builtin_amdgcn_readfirstlane(n / X);
+  const int C = __builtin_amdgcn_readfirstlane(((int)gridDim.x - x + X - 1) / X);
+  const int PX = __builtin_amdgcn_readfirstlane(((p.BH - x + X - 1) / X) * p.npairs);
+  const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
+
+  for (int pp = c; pp < PX; pp += C) {
+  const int hl = __builtin_amdgcn_readfirstlane(pp / p.npairs);
+  const int j_pair = pp - hl * p.npairs;
+  const int bh = x + X * hl;
+  for (int half = 0; half < 2; ++half) {
+  if (half == 1 && p.nqb - 1 - j_pair == j_pair) break;   // odd block count: middle block alone
+  const int qb = half == 0 ? p.nqb - 1 - j_pair : j_pair;
+  const int i0 = __builtin_amdgcn_readfirstlane(qb * kBM);
+
+  const size_t qbase = (size_t)bh * (size_t)p.Tq * D;
+  const size_t kbase = (size_t)bh * (size_t)p.Tk * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qbase, (uint32_t)p.Tq * D * 2u);
+  const u32x4_t rk = rsrc_words(p.k + kbase, (uint32_t)p.Tk * D * 2u);
+  const u32x4_t rv = rsrc_words(p.v + kbase, (uint32_t)p.Tk * D * 2u);
+
+  // ---- this wave's 32 query rows; Q fragment kept in registers ----
+  const int qw0 = i0 + wave * 32;
+  const int qrow = qw0 + r32;
+  const int qw_last = min(qw0 + 31, p.Tq - 1);
+  const bool wave_has_rows = qw0 < p.Tq;
+  bf16x8_t qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
+    w ^= p.q_sign;
+    qf[s] = as_bf16x8(w);
+  }
+
+  // keys the workgroup needs: all, or (causal) up to the block's last row
+  int kend = p.Tk;
+  if (CAUSAL) kend = min(p.Tk, min(i0 + kBM, p.Tq) + off);
+  const int ntiles = __builtin_amdgcn_readfirstlane((kend + kBN - 1) / kBN);
+
+  auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
+
   float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
-  float l_run = 0.f;         // this lane's partial running sum of p (fp32): the LSE
-  float l16_run = 0.f;       // this lane's partial running sum of bf16(p): normalises O
+  float m_thr = -INFINITY;   // m_run + rescale threshold
+  // This lane's running sums, kept as four partial sums each (independent add chains):
+  float l_run[4] = {0.f, 0.f, 0.f, 0.f};     // of p (fp32): the LSE
+  float l16_run[4] = {0.f, 0.f, 0.f, 0.f};   // of bf16(p): normalises O
   f32x16_t oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x16_t{};
@@ -287,81 +301,94 @@ void fa_fwd_kernel(FwdParams p) {
   __syncthreads();
   if (group_b) __syncthreads();   // group B runs one section behind group A
 
+  // ---- matrix-section operands ----
+  // A section is a list of MFMAs whose A operands stream from LDS through a ring of kRing
+  // registers, each read issued kRing MFMAs ahead of its use.  Section t (t >= 1) applies the
+  // previous tile's P^T (O^T += V^T P^T, operands: V^T of tile t - 1) and computes this tile's
+  // scores (S^T = K Q^T, operands: K of tile t), in the order: first half of the V^T operands,
+  // all K operands, second half of the V^T operands.  Section 0 has only the scores.
+  //  * The leading V^T operands may be read by a wave as soon as its own vector section t - 1
+  //    has run (tile t - 1 was published two barriers earlier), so they are issued at the end of
+  //    that vector section and their latency hides behind the barrier.
+  //  * The scores are finished half a section before its end, so the vector section that follows
+  //    does not wait for the matrix pipe to drain.
+  constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
+  constexpr int VH = NV / 2;                        // V^T operands before the scores
+  constexpr int PRE = VH < kRing ? VH : kRing;      // of which read ahead of the barrier
+  bf16x8_t ring[kRing];
+  // K operand kk: rows 32*(kk%2) + r32, k-step kk/2 of the tile at ks.
+  auto k_opnd = [&](uint32_t ks, int kk) -> bf16x8_t {
+    return lds_read16((ks ^ (32u * (kk >> 1))) + 2 * 32 * (kk & 1) * D);
+  };
+  // V^T operand j: block db = j%ND, k-step j/ND of the tile at vs (two transposing reads).
+  auto v_opnd = [&](uint32_t vs, int j) -> bf16x8_t {
+    const uint32_t base = (vs ^ (64u * (j % ND))) + 2 * 16 * (j / ND) * D;
+    const u32x2_t lo = lds_read_tr(base);
+    const u32x2_t hi = lds_read_tr(base + 2 * 8 * D);
+    const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+    return as_bf16x8(w);
+  };
+  auto k_at = [&](int x) { return k_base + (uint32_t)(x % kStages) * kTileBytes; };
+  auto v_at = [&](int x) { return v_base + (uint32_t)(x % kStages) * kTileBytes; };
+
+  // ring[0 .. PRE-1] (FULL) or ring[0 .. kRing-1] (scores only) hold the first operands on entry.
+  auto section = [&](auto full, uint32_t ks, uint32_t vs) {
+    constexpr bool F = decltype(full)::value;
+    constexpr int vh = F ? VH : 0, n = F ? NV + NK : NK;
+    constexpr int pre = F ? PRE : kRing;
+    auto is_k = [&](int i) { return i >= vh && i < vh + NK; };
+    auto opnd = [&](int i) {
+      return i < vh ? v_opnd(vs, i) : (i < vh + NK ? k_opnd(ks, i - vh) : v_opnd(vs, i - NK));
+    };
+#pragma unroll
+    for (int i = pre; i < kRing; ++i) ring[i] = opnd(i);   // (K operands)
+    sacc[0] = f32x16_t{};
+    sacc[1] = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const bf16x8_t a = ring[i % kRing];
+      if (i + kRing < n) ring[i % kRing] = opnd(i + kRing);
+      if (is_k(i)) {
+        const int kk = i - vh;
+        sacc[kk & 1] = mfma_32x32x16(a, qf[kk >> 1], sacc[kk & 1]);
+      } else {
+        const int j = i < vh ? i : i - NK;
+        oacc[j % ND] = mfma_32x32x16(a, pb[j / ND], oacc[j % ND]);
+      }
+    }
+    // the remaining initial reads, then (MFMA, refill reads) pairs, then the last kRing MFMAs
+    if (pre < kRing) __builtin_amdgcn_sched_group_barrier(0x100, kRing - pre, 0);
+    constexpr int k_lo = kRing > vh ? kRing : vh, k_hi = vh + NK;   // refills that are K
+#pragma unroll
+    for (int r = kRing; r < vh; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int r = k_lo; r < k_hi; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int r = k_hi > kRing ? k_hi : kRing; r < n; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
+  };
+
   auto step = [&](const int t, auto first_step) {
     // ================= matrix section =================
     __builtin_amdgcn_s_setprio(1);
     request(t + 2);
-    {
-      // Operands stream through a ring of kRing LDS reads issued ahead of the MFMAs that use
-      // them: first the 2*NS K operands of S^T = K Q^T, then the 4*ND V^T operands of
-      // O^T += V^T P^T.  The two cases (S^T only on the first tile, both products after it)
-      // are separate compile-time instances so every ring index is static.
-      constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
-      const uint32_t ks = k_base + (uint32_t)(t % kStages) * kTileBytes;              // tile t
-      const uint32_t vs = v_base + (uint32_t)((t + kStages - 1) % kStages) * kTileBytes;  // t - 1
-      // operand i < NK: K rows 32*(i%2) + r32, k-step i/2; i >= NK: V^T block db = j%ND, k-step
-      // ks = j/ND with j = i - NK (two transposing reads).
-      auto opnd = [&](int i) -> bf16x8_t {
-        if (i < NK) return lds_read16((ks ^ (32u * (i >> 1))) + 2 * 32 * (i & 1) * D);
-        const int j = i - NK;
-        const uint32_t base = (vs ^ (64u * (j % ND))) + 2 * 16 * (j / ND) * D;
-        const u32x2_t lo = lds_read_tr(base);
-        const u32x2_t hi = lds_read_tr(base + 2 * 8 * D);
-        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-        return as_bf16x8(w);
-      };
-      auto section = [&](auto with_s, auto with_o) {
-        constexpr int first = decltype(with_s)::value ? 0 : NK;
-        constexpr int last = decltype(with_o)::value ? NK + NV : NK;
-        bf16x8_t ring[kRing];
-#pragma unroll
-        for (int i = 0; i < kRing; ++i)
-          if (first + i < last) ring[i] = opnd(first + i);
-        if (decltype(with_s)::value) {
-          sacc[0] = f32x16_t{};
-          sacc[1] = f32x16_t{};
-        }
-#pragma unroll
-        for (int i = first; i < last; ++i) {
-          const bf16x8_t a = ring[(i - first) % kRing];
-          if (i + kRing < last) ring[(i - first) % kRing] = opnd(i + kRing);
-          if (i < NK) {
-            sacc[i & 1] = mfma_32x32x16(a, qf[i >> 1], sacc[i & 1]);
-          } else {
-            const int j = i - NK;
-            oacc[j % ND] = mfma_32x32x16(a, pb[j / ND], oacc[j % ND]);
-          }
-        }
-        // keep the operand reads ahead of the MFMAs: reads for the first kRing operands, then
-        // (MFMA, reads) pairs, then the last MFMAs
-        constexpr int n = last - first;
-        constexpr int ahead = n < kRing ? n : kRing;
-        constexpr int nk_in = first == 0 ? (NK < ahead ? NK : ahead) : 0;
-        __builtin_amdgcn_sched_group_barrier(0x100, nk_in + 2 * (ahead - nk_in), 0);
-        constexpr int k_after = NK - first - ahead > 0 ? NK - first - ahead : 0;   // K reads
-#pragma unroll
-        for (int i = 0; i < k_after; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = k_after; i < n - ahead; ++i) {   // V^T operands: two transposing reads
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
-      };
-      // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
-      // that has the previous tile's P^T to apply runs both products; at the step after its last
-      // tile the S^T product is wasted (and ignored), which keeps a single code path for the
-      // accumulators.
-      using yes = std::true_type;
-      using no = std::false_type;
-      if (decltype(first_step)::value) {
-        if (active(0)) section(yes{}, no{});
-      } else {
-        if (active(t - 1)) section(yes{}, yes{});
-      }
+    // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
+    // that has the previous tile's P^T to apply runs both products; at the step after its last
+    // tile the S^T product is wasted (and ignored), which keeps a single code path for the
+    // accumulators.
+    if (decltype(first_step)::value) {
+      if (active(0)) section(std::false_type{}, k_at(0), 0u);
+    } else {
+      if (active(t - 1)) section(std::true_type{}, k_at(t), v_at(t - 1));
     }
     wait_next(t);
     __builtin_amdgcn_s_setprio(0);
@@ -391,29 +418,30 @@ void fa_fwd_kernel(FwdParams p) {
       float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
       mt = xhalf_max(mt) * p.scale_log2;
       // lazy rescale: only when some row's max outgrew the max in use by > 2^8
-      if (__any(mt > m_run + kRescaleThreshold)) {
+      if (__any(mt > m_thr)) {
         const float m_new = fmaxf(m_run, mt);
         const float corr = fast_exp2(m_run - m_new);
-        l_run *= corr;
-        l16_run *= corr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          l_run[c] *= corr;
+          l16_run[c] *= corr;
+        }
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
         m_run = m_new;
+        m_thr = m_new + kRescaleThreshold;
       }
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
           sacc[kb][i] = e;
-          ps[i & 3] += e;
+          l_run[i & 3] += e;
         }
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
-      float l16[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const f32x16_t& sb = sacc[ks >> 1];
@@ -424,22 +452,27 @@ void fa_fwd_kernel(FwdParams p) {
         pb[ks] = as_bf16x8(w);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          l16[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(), l16[e],
-                                                   false);
+          l16_run[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(),
+                                                       l16_run[e], false);
       }
-      l16_run += (l16[0] + l16[1]) + (l16[2] + l16[3]);
+      // the next section's leading operands: V^T of this tile
+#pragma unroll
+      for (int i = 0; i < PRE; ++i) ring[i] = v_opnd(v_at(t), i);
     }
     __syncthreads();
   };
+  // section 0's first operands: K of tile 0
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) ring[i] = k_opnd(k_at(0), i);
   step(0, std::true_type{});
   for (int t = 1; t <= ntiles; ++t) step(t, std::false_type{});
   if (!group_b) __syncthreads();   // match group B's extra barrier
 
   // ---- epilogue: O = acc / l16, LSE = (m + log2 l) * ln 2 ----
-  if (!wave_has_rows) return;
-  const float l_tot = xhalf_sum(l_run);
-  const float l16_tot = xhalf_sum(l16_run);
-  if (qrow >= p.Tq) return;
+  // (no LDS access: the next item's prologue may start filling stages right away)
+  const float l_tot = xhalf_sum((l_run[0] + l_run[1]) + (l_run[2] + l_run[3]));
+  const float l16_tot = xhalf_sum((l16_run[0] + l16_run[1]) + (l16_run[2] + l16_run[3]));
+  if (wave_has_rows && qrow < p.Tq) {
   const float inv = 1.0f / l16_tot;
   const size_t orow = qbase + (size_t)qrow * D;
 #pragma unroll
@@ -459,6 +492,9 @@ void fa_fwd_kernel(FwdParams p) {
     }
   }
   if (g == 0) p.lse[(size_t)bh * p.Tq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+  }   // half
+  }   // pair
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
@@ -472,13 +508,30 @@ hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
   p.Tq = a.Tq;
   p.Tk = a.Tk;
   p.nqb = (a.Tq + kBM - 1) / kBM;
-  p.total_wg = p.nqb * a.B * a.H;
+  p.BH = a.B * a.H;
+  p.npairs = (p.nqb + 1) / 2;
   // A zero scale would make every score 0; a tiny positive factor gives the same softmax.
   p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  // One workgroup per CU (each needs a whole CU's LDS), in 8 groups (one per XCD) when there
+  // are more block pairs than CUs; otherwise one workgroup per pair.
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long pairs = (long long)p.BH * p.npairs;
+  int grid;
+  if (pairs > cus && cus >= 8) {
+    p.groups = 8;
+    grid = cus - cus % 8;
+  } else {
+    p.groups = 1;
+    grid = (int)(pairs < cus ? pairs : (cus > 0 ? cus : 1));
+  }
   void* args[] = {&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, OUT_F32>),
-                         dim3(p.total_wg), dim3(kThreads), args, 0, stream);
+                         dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 template <int D>
