@@ -105,6 +105,11 @@ struct Tile {
 // Loads one wave issues per tile (K and V).
 template <int D>
 constexpr int kVmcntTile = vmcnt_imm(2 * Tile<D>::LOADS_PER_WAVE);
+// ... plus the D/16 loads of a wave's Q rows.
+template <int D>
+constexpr int kVmcntQ = vmcnt_imm(D / 16);
+template <int D>
+constexpr int kVmcntQTile = vmcnt_imm(D / 16 + 2 * Tile<D>::LOADS_PER_WAVE);
 
 // One buffer_load_dwordx4 ... lds: lane l reads 16 bytes at byte offset voff of the buffer
 // (zeros past its end) and writes them to LDS bytes [m0 + 16*l, m0 + 16*l + 16).  Written as
@@ -127,6 +132,44 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) 
   return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
+// Matrix sections (see the kernel): scores only (first tile of a block), both products, or the
+// P^T product only (after the last tile).
+constexpr int kSecScores = 0, kSecBoth = 1, kSecValues = 2;
+constexpr int kRing = 8;   // operand registers in flight per matrix section
+
+// Operand order of a matrix section: scores only = the NK K operands; both = VH V^T operands,
+// the NK K operands, the other NV - VH V^T operands; values only = the NV V^T operands.  kPre
+// operands are in the ring on entry.  K operands take one LDS read, V^T operands two.
+template <int MODE, int NV, int NK, int VH>
+struct OpSeq {
+  static constexpr int n = MODE == kSecScores ? NK : (MODE == kSecBoth ? NV + NK : NV);
+  static constexpr bool kScores = MODE != kSecValues;
+  static constexpr int kPre = MODE == kSecScores ? kRing : (VH < kRing ? VH : kRing);
+  static constexpr __device__ bool is_k(int i) {
+    return MODE == kSecScores || (MODE == kSecBoth && i >= VH && i < VH + NK);
+  }
+  static constexpr __device__ int k_index(int i) { return MODE == kSecScores ? i : i - VH; }
+  static constexpr __device__ int v_index(int i) {
+    return MODE == kSecBoth && i >= VH + NK ? i - NK : i;
+  }
+  static constexpr __device__ int reads(int i) { return is_k(i) ? 1 : 2; }
+  static constexpr __device__ int initial_reads() {
+    int r = 0;
+    for (int i = kPre; i < kRing && i < n; ++i) r += reads(i);
+    return r;
+  }
+};
+
+// Scheduling pattern of a section's steady state: MFMA i, then the reads of operand i + kRing.
+template <class S, int R>
+__device__ __forceinline__ void sched_refills() {
+  if constexpr (R < S::n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, S::reads(R), 0);
+    sched_refills<S, R + 1>();
+  }
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j receives,
 // for t = 0..3, the 16-bit element j % 4 of the 8 bytes addressed by lane 4t + j / 4.
 __device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
@@ -134,6 +177,16 @@ __device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
   typedef __attribute__((address_space(3))) s16x4_t* lds_ptr_t;
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16- and 8-byte LDS accesses at a byte address.
+__device__ __forceinline__ u32x4_t lds_read16u(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const u32x4_t* lds_ptr_t;
+  return *(lds_ptr_t)(uintptr_t)addr;
+}
+__device__ __forceinline__ void lds_write8(uint32_t addr, u32x2_t v) {
+  typedef __attribute__((address_space(3))) u32x2_t* lds_ptr_t;
+  *(lds_ptr_t)(uintptr_t)addr = v;
 }
 
 // 16-byte LDS read at a byte address.
@@ -170,10 +223,15 @@ void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
   constexpr int NS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int ND = D / 32;   // 32-row blocks of O^T
+  constexpr int NK = 2 * NS, NV = 4 * ND;            // K and V^T operands per tile
+  constexpr int VH = NV / 2;                         // V^T operands before the scores
+  constexpr int PRE = VH < kRing ? VH : kRing;       // of which read ahead of the barrier
   // LDS: the four K stages, then the four V stages.  Every access below is a per-lane base
   // address (fixed for the whole kernel) plus a compile-time offset below 64 KB, which the
   // LDS instructions take as an immediate.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
+  // Output staging: 32 rows x 64 columns of bf16 per wave (the rest of the CU's 160 KB).
+  __shared__ __attribute__((aligned(1024))) uint16_t ostage[kWaves * 32 * 64];
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   constexpr uint32_t kTileBytes = T::TILE * 2, kVRegion = kStages * kTileBytes;
 
@@ -217,104 +275,81 @@ void fa_fwd_kernel(FwdParams p) {
   // (the XCD it is dispatched to) and takes heads x, x + groups, ... of that group; the group's
   // (head, block pair) list is dealt round-robin over its workgroups, so the workgroups of one
   // XCD work on a few heads at a time and share their K/V in that XCD's L2.  A pair holds query
-  // blocks nqb-1-j and j, whose causal costs add up to the same total for every j.
+  // blocks nqb-1-j and j, whose causal costs add up to the same total for every j.  A workgroup
+  // runs its items (one query block each) back to back as one stream of K/V tiles: the first
+  // tiles and the Q rows of the next item are loaded while the current one finishes.
   const int n = blockIdx.x, X = p.groups;
   const int x = __builtin_amdgcn_readfirstlane(n % X), c = __builtin_amdgcn_readfirstlane(n / X);
   const int C = __builtin_amdgcn_readfirstlane(((int)gridDim.x - x + X - 1) / X);
   const int PX = __builtin_amdgcn_readfirstlane(((p.BH - x + X - 1) / X) * p.npairs);
   const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
 
-  for (int pp = c; pp < PX; pp += C) {
-  const int hl = __builtin_amdgcn_readfirstlane(pp / p.npairs);
-  const int j_pair = pp - hl * p.npairs;
-  const int bh = x + X * hl;
-  for (int half = 0; half < 2; ++half) {
-  if (half == 1 && p.nqb - 1 - j_pair == j_pair) break;   // odd block count: middle block alone
-  const int qb = half == 0 ? p.nqb - 1 - j_pair : j_pair;
-  const int i0 = __builtin_amdgcn_readfirstlane(qb * kBM);
-
-  const size_t qbase = (size_t)bh * (size_t)p.Tq * D;
-  const size_t kbase = (size_t)bh * (size_t)p.Tk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qbase, (uint32_t)p.Tq * D * 2u);
-  const u32x4_t rk = rsrc_words(p.k + kbase, (uint32_t)p.Tk * D * 2u);
-  const u32x4_t rv = rsrc_words(p.v + kbase, (uint32_t)p.Tk * D * 2u);
-
-  // ---- this wave's 32 query rows; Q fragment kept in registers ----
-  const int qw0 = i0 + wave * 32;
-  const int qrow = qw0 + r32;
-  const int qw_last = min(qw0 + 31, p.Tq - 1);
-  const bool wave_has_rows = qw0 < p.Tq;
+  struct Item {
+    int pp, half;   // pair index in the group, 0 = block nqb-1-j / 1 = block j
+    int bh, i0, ntiles;
+  };
+  auto describe = [&](int pp, int half) {
+    Item it;
+    it.pp = pp;
+    it.half = half;
+    const int hl = __builtin_amdgcn_readfirstlane(pp / p.npairs);
+    const int j = pp - hl * p.npairs;
+    it.bh = x + X * hl;
+    it.i0 = __builtin_amdgcn_readfirstlane((half == 0 ? p.nqb - 1 - j : j) * kBM);
+    // keys the block needs: all, or (causal) up to its last row
+    int kend = p.Tk;
+    if (CAUSAL) kend = min(p.Tk, min(it.i0 + kBM, p.Tq) + off);
+    it.ntiles = __builtin_amdgcn_readfirstlane((kend + kBN - 1) / kBN);
+    return it;
+  };
+  auto following = [&](const Item& it) {   // (pp >= PX: no item)
+    const int j = it.pp - (it.pp / p.npairs) * p.npairs;
+    if (it.half == 0 && p.nqb - 1 - j != j) return describe(it.pp, 1);
+    return describe(it.pp + C, 0);
+  };
+  auto k_rsrc = [&](const Item& it) {
+    return rsrc_words(p.k + (size_t)it.bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+  };
+  auto v_rsrc = [&](const Item& it) {
+    return rsrc_words(p.v + (size_t)it.bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+  };
+  // this wave's 32 query rows of an item, as the B operand fragment of S^T = K Q^T
   bf16x8_t qf[NS];
+  auto load_q = [&](const Item& it) {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(p.q + (size_t)it.bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
+    const int qrow = it.i0 + wave * 32 + r32;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
-    w ^= p.q_sign;
-    qf[s] = as_bf16x8(w);
-  }
-
-  // keys the workgroup needs: all, or (causal) up to the block's last row
-  int kend = p.Tk;
-  if (CAUSAL) kend = min(p.Tk, min(i0 + kBM, p.Tq) + off);
-  const int ntiles = __builtin_amdgcn_readfirstlane((kend + kBN - 1) / kBN);
-
-  auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
-
-  float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
-  float m_thr = -INFINITY;   // m_run + rescale threshold
-  // This lane's running sums, kept as four partial sums each (independent add chains):
-  float l_run[4] = {0.f, 0.f, 0.f, 0.f};     // of p (fp32): the LSE
-  float l16_run[4] = {0.f, 0.f, 0.f, 0.f};   // of bf16(p): normalises O
-  f32x16_t oacc[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) oacc[db] = f32x16_t{};
-  f32x16_t sacc[2];
-  bf16x8_t pb[4];
-
-  // Tile x occupies stage x % 4.  Tile x + 2 is requested at the start of matrix section x;
-  // each wave waits for its own part of tile x + 1 at the end of matrix section x (one more
-  // tile may still be in flight), and the barrier that follows publishes it to all waves.
-  auto request = [&](int x) {
-    if (x < ntiles) {
-      const uint32_t so = (uint32_t)(x % kStages) * kTileBytes;
-      const uint32_t g0 = (uint32_t)x * (kBN * D * 2);
-#pragma unroll
-      for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
-        const uint32_t piece = (uint32_t)(wave * T::LOADS_PER_WAVE + i) * 1024u;
-        lds_dma16(rk, lds0 + so + piece, g0 + dk[i]);
-        lds_dma16(rv, lds0 + kVRegion + so + piece, g0 + dv[i]);
-      }
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
+      w ^= p.q_sign;
+      qf[s] = as_bf16x8(w);
     }
   };
-  auto wait_next = [&](int x) {   // tile x + 1 has landed (this wave's part)
-    if (x + 2 < ntiles)
-      __builtin_amdgcn_s_waitcnt(kVmcntTile<D>);
-    else
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  // one K/V tile of an item into stage st
+  auto dma = [&](u32x4_t rk, u32x4_t rv, int tile, int st) {
+    const uint32_t g0 = (uint32_t)tile * (kBN * D * 2);
+    const uint32_t so = (uint32_t)st * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+      const uint32_t piece = (uint32_t)(wave * T::LOADS_PER_WAVE + i) * 1024u;
+      lds_dma16(rk, lds0 + so + piece, g0 + dk[i]);
+      lds_dma16(rv, lds0 + kVRegion + so + piece, g0 + dv[i]);
+    }
   };
-
-  // ---- prologue: Q and tiles 0 and 1 loaded and published ----
-  // (a full wait: it also settles the Q loads, which the compiler would otherwise wait for at
-  // their first use, behind the next tile's loads)
-  request(0);
-  request(1);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-  if (group_b) __syncthreads();   // group B runs one section behind group A
 
   // ---- matrix-section operands ----
   // A section is a list of MFMAs whose A operands stream from LDS through a ring of kRing
-  // registers, each read issued kRing MFMAs ahead of its use.  Section t (t >= 1) applies the
-  // previous tile's P^T (O^T += V^T P^T, operands: V^T of tile t - 1) and computes this tile's
-  // scores (S^T = K Q^T, operands: K of tile t), in the order: first half of the V^T operands,
-  // all K operands, second half of the V^T operands.  Section 0 has only the scores.
+  // registers, each read issued kRing MFMAs ahead of its use.  Section t (1 <= t < ntiles)
+  // applies the previous tile's P^T (O^T += V^T P^T, operands: V^T of tile t - 1) and computes
+  // this tile's scores (S^T = K Q^T, operands: K of tile t), in the order: first half of the
+  // V^T operands, all K operands, second half of the V^T operands.  Section 0 has only the
+  // scores, section ntiles only the P^T product.
   //  * The leading V^T operands may be read by a wave as soon as its own vector section t - 1
   //    has run (tile t - 1 was published two barriers earlier), so they are issued at the end of
   //    that vector section and their latency hides behind the barrier.
   //  * The scores are finished half a section before its end, so the vector section that follows
   //    does not wait for the matrix pipe to drain.
-  constexpr int NK = 2 * NS, NV = 4 * ND, kRing = 8;
-  constexpr int VH = NV / 2;                        // V^T operands before the scores
-  constexpr int PRE = VH < kRing ? VH : kRing;      // of which read ahead of the barrier
   bf16x8_t ring[kRing];
   // K operand kk: rows 32*(kk%2) + r32, k-step kk/2 of the tile at ks.
   auto k_opnd = [&](uint32_t ks, int kk) -> bf16x8_t {
@@ -328,173 +363,272 @@ void fa_fwd_kernel(FwdParams p) {
     const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
     return as_bf16x8(w);
   };
-  auto k_at = [&](int x) { return k_base + (uint32_t)(x % kStages) * kTileBytes; };
-  auto v_at = [&](int x) { return v_base + (uint32_t)(x % kStages) * kTileBytes; };
+  auto k_at = [&](int st) { return k_base + (uint32_t)st * kTileBytes; };
+  auto v_at = [&](int st) { return v_base + (uint32_t)st * kTileBytes; };
 
-  // ring[0 .. PRE-1] (FULL) or ring[0 .. kRing-1] (scores only) hold the first operands on entry.
-  auto section = [&](auto full, uint32_t ks, uint32_t vs) {
-    constexpr bool F = decltype(full)::value;
-    constexpr int vh = F ? VH : 0, n = F ? NV + NK : NK;
-    constexpr int pre = F ? PRE : kRing;
-    auto is_k = [&](int i) { return i >= vh && i < vh + NK; };
+  f32x16_t oacc[ND];
+  f32x16_t sacc[2];
+  bf16x8_t pb[4];
+  // On entry ring[0 .. kPre-1] hold the first operands (kPre: kRing for scores only, else PRE).
+  auto section = [&](auto mode, uint32_t ks, uint32_t vs) {
+    using S = OpSeq<decltype(mode)::value, NV, NK, VH>;
+    constexpr int pre = S::kPre;
     auto opnd = [&](int i) {
-      return i < vh ? v_opnd(vs, i) : (i < vh + NK ? k_opnd(ks, i - vh) : v_opnd(vs, i - NK));
+      return S::is_k(i) ? k_opnd(ks, S::k_index(i)) : v_opnd(vs, S::v_index(i));
     };
 #pragma unroll
-    for (int i = pre; i < kRing; ++i) ring[i] = opnd(i);   // (K operands)
-    sacc[0] = f32x16_t{};
-    sacc[1] = f32x16_t{};
+    for (int i = pre; i < kRing; ++i) ring[i] = opnd(i);
+    if (S::kScores) {
+      sacc[0] = f32x16_t{};
+      sacc[1] = f32x16_t{};
+    }
 #pragma unroll
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < S::n; ++i) {
       const bf16x8_t a = ring[i % kRing];
-      if (i + kRing < n) ring[i % kRing] = opnd(i + kRing);
-      if (is_k(i)) {
-        const int kk = i - vh;
+      if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+      if (S::is_k(i)) {
+        const int kk = S::k_index(i);
         sacc[kk & 1] = mfma_32x32x16(a, qf[kk >> 1], sacc[kk & 1]);
       } else {
-        const int j = i < vh ? i : i - NK;
+        const int j = S::v_index(i);
         oacc[j % ND] = mfma_32x32x16(a, pb[j / ND], oacc[j % ND]);
       }
     }
     // the remaining initial reads, then (MFMA, refill reads) pairs, then the last kRing MFMAs
-    if (pre < kRing) __builtin_amdgcn_sched_group_barrier(0x100, kRing - pre, 0);
-    constexpr int k_lo = kRing > vh ? kRing : vh, k_hi = vh + NK;   // refills that are K
-#pragma unroll
-    for (int r = kRing; r < vh; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int r = k_lo; r < k_hi; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int r = k_hi > kRing ? k_hi : kRing; r < n; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+    if (S::initial_reads() > 0) __builtin_amdgcn_sched_group_barrier(0x100, S::initial_reads(), 0);
+    sched_refills<S, kRing>();
     __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
   };
+  using ScoresOnly = std::integral_constant<int, kSecScores>;
+  using Both = std::integral_constant<int, kSecBoth>;
+  using ValuesOnly = std::integral_constant<int, kSecValues>;
 
-  auto step = [&](const int t, auto first_step) {
-    // ================= matrix section =================
-    __builtin_amdgcn_s_setprio(1);
-    request(t + 2);
-    // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
-    // that has the previous tile's P^T to apply runs both products; at the step after its last
-    // tile the S^T product is wasted (and ignored), which keeps a single code path for the
-    // accumulators.
-    if (decltype(first_step)::value) {
-      if (active(0)) section(std::false_type{}, k_at(0), 0u);
-    } else {
-      if (active(t - 1)) section(std::true_type{}, k_at(t), v_at(t - 1));
+  Item cur = describe(c, 0);
+  int g0 = 0;   // stream position of the current item's tile 0 (tile x sits in stage x % 4)
+  if (cur.pp < PX) {
+    // ---- prologue: Q and the first two tiles of the stream loaded and published ----
+    load_q(cur);
+    {
+      const u32x4_t rk = k_rsrc(cur), rv = v_rsrc(cur);
+      dma(rk, rv, 0, 0);
+      if (cur.ntiles > 1) {
+        dma(rk, rv, 1, 1);
+      } else {
+        const Item nx = following(cur);
+        if (nx.pp < PX) dma(k_rsrc(nx), v_rsrc(nx), 0, 1);
+      }
     }
-    wait_next(t);
-    __builtin_amdgcn_s_setprio(0);
+    // (a full wait: it also settles the Q loads, which the compiler would otherwise wait for
+    // at their first use, behind later tile loads)
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
+    if (group_b) __syncthreads();   // group B runs one section behind group A
+  }
 
-    // ================= vector section =================
-    if (t < ntiles && active(t)) {
-      const int j0 = t * kBN;
-      const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+  while (cur.pp < PX) {
+    const Item nxt = following(cur);
+    const bool has_nxt = nxt.pp < PX;
+    const int ntiles = cur.ntiles;
+    const u32x4_t rk = k_rsrc(cur), rv = v_rsrc(cur);
+    const u32x4_t rk_n = k_rsrc(nxt), rv_n = v_rsrc(nxt);
+
+    const int qw0 = cur.i0 + wave * 32;
+    const int qrow = qw0 + r32;
+    const int qw_last = min(qw0 + 31, p.Tq - 1);
+    const bool wave_has_rows = qw0 < p.Tq;
+    auto active = [&](int t) { return wave_has_rows && !(CAUSAL && t * kBN > qw_last + off); };
+
+    float m_run = -INFINITY;   // running max used for the exponentials (log2 units)
+    float m_thr = -INFINITY;   // m_run + rescale threshold
+    // This lane's running sums, kept as four partial sums each (independent add chains):
+    float l_run[4] = {0.f, 0.f, 0.f, 0.f};     // of p (fp32): the LSE
+    float l16_run[4] = {0.f, 0.f, 0.f, 0.f};   // of bf16(p): normalises O
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] = f32x16_t{};
+
+    // Stream tile x of this item (x >= ntiles: tile x - ntiles of the next item).  Tile x + 2 is
+    // requested at the start of matrix section x; each wave waits for its own part of tile
+    // x + 1 at the end of matrix section x (one more tile may still be in flight), and the
+    // barrier that follows publishes it to all waves.
+    auto exists = [&](int xt) { return xt < ntiles || (has_nxt && xt - ntiles < nxt.ntiles); };
+    auto request = [&](int xt) {
+      const int st = (g0 + xt) & (kStages - 1);
+      if (xt < ntiles) dma(rk, rv, xt, st);
+      else if (exists(xt)) dma(rk_n, rv_n, xt - ntiles, st);
+    };
+    // Vector-memory operations complete in issue order.  Before tile 1 of an item has landed,
+    // the previous item's last step issued this item's Q rows and the previous output stores,
+    // after tile 1's loads; allowing the Q loads to stay in flight keeps the stores (the younger
+    // part) out of the wait as well.  (For the first item, tiles 0 and 1 were waited for fully.)
+    auto wait_next = [&](int t) {   // stream tile t + 1 has landed (this wave's part)
+      if (t == 0) {
+        if (exists(2))
+          __builtin_amdgcn_s_waitcnt(kVmcntQTile<D>);
+        else
+          __builtin_amdgcn_s_waitcnt(kVmcntQ<D>);
+      } else if (exists(t + 2)) {
+        __builtin_amdgcn_s_waitcnt(kVmcntTile<D>);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      }
+    };
+
+    auto step = [&](const int t, auto mode) {
+      constexpr int MODE = decltype(mode)::value;
+      const int st = (g0 + t) & (kStages - 1), st_prev = (g0 + t + kStages - 1) & (kStages - 1);
+      // ================= matrix section =================
+      __builtin_amdgcn_s_setprio(1);
+      request(t + 2);
+      // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
+      // that has the previous tile's P^T to apply runs both products; at the step after its
+      // last tile the S^T product is wasted (and ignored), which keeps a single code path for
+      // the accumulators.
+      if (MODE == kSecScores) {
+        if (active(0)) section(ScoresOnly{}, k_at(st), 0u);
+      } else {
+        if (active(t - 1)) section(Both{}, k_at(st), v_at(st_prev));
+      }
+      wait_next(t);
+      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();
+
+      // ================= vector section =================
+      if (active(t)) {
+        const int j0 = t * kBN;
+        const bool need_mask = (j0 + kBN > p.Tk) || (CAUSAL && j0 + kBN - 1 > qw0 + off);
+        if (need_mask) {
+          const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key > lim) sacc[kb][i] = -INFINITY;
+            }
+        }
+        // Every reduction below runs as four independent chains: one wave per SIMD does this
+        // work while the other issues MFMAs, so dependent-issue latency is not hidden by others.
+        float mx[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) mx[cc] = fmaxf(sacc[0][cc], sacc[0][cc + 4]);
+#pragma unroll
+        for (int i = 8; i < 32; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[i >> 4][i & 15]);
+        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        mt = xhalf_max(mt) * p.scale_log2;
+        // lazy rescale: only when some row's max outgrew the max in use by > 2^8
+        if (__any(mt > m_thr)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float corr = fast_exp2(m_run - m_new);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            l_run[cc] *= corr;
+            l16_run[cc] *= corr;
+          }
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+          m_run = m_new;
+          m_thr = m_new + kRescaleThreshold;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > lim) sacc[kb][i] = -INFINITY;
+            const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
+            sacc[kb][i] = e;
+            l_run[i & 3] += e;
           }
-      }
-      // Every reduction below runs as four independent chains: one wave per SIMD does this
-      // work while the other issues MFMAs, so dependent-issue latency is not hidden by others.
-      float mx[4];
+        // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mx[c] = fmaxf(sacc[0][c], sacc[0][c + 4]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x16_t& sb = sacc[ks >> 1];
+          const int b0 = (ks & 1) * 8;
+          const u32x2_t lo = pack_bf16x4(sb[b0], sb[b0 + 1], sb[b0 + 2], sb[b0 + 3]);
+          const u32x2_t hi = pack_bf16x4(sb[b0 + 4], sb[b0 + 5], sb[b0 + 6], sb[b0 + 7]);
+          u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+          pb[ks] = as_bf16x8(w);
 #pragma unroll
-      for (int i = 8; i < 32; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[i >> 4][i & 15]);
-      float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-      mt = xhalf_max(mt) * p.scale_log2;
-      // lazy rescale: only when some row's max outgrew the max in use by > 2^8
-      if (__any(mt > m_thr)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float corr = fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          l_run[c] *= corr;
-          l16_run[c] *= corr;
+          for (int e = 0; e < 4; ++e)
+            l16_run[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(),
+                                                         l16_run[e], false);
         }
+        // the next section's leading operands: V^T of this tile
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) ring[i] = v_opnd(v_at(st), i);
+      }
+      __syncthreads();
+    };
+
+    // section 0's first operands: K of tile 0
+    {
+      const uint32_t ks0 = k_at(g0 & (kStages - 1));
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) ring[i] = k_opnd(ks0, i);
+    }
+    step(0, ScoresOnly{});
+    for (int t = 1; t < ntiles; ++t) step(t, Both{});
+
+    // ---- last step: the last tile's P^T, then the epilogue in the vector slot ----
+    __builtin_amdgcn_s_setprio(1);
+    if (active(ntiles - 1))
+      section(ValuesOnly{}, 0u, v_at((g0 + ntiles - 1) & (kStages - 1)));
+    if (has_nxt) load_q(nxt);   // the S^T fragment is free from here on
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
+    // O = acc / l16, LSE = (m + log2 l) * ln 2 (touches only this wave's output staging)
+    const float l_tot = xhalf_sum((l_run[0] + l_run[1]) + (l_run[2] + l_run[3]));
+    const float l16_tot = xhalf_sum((l16_run[0] + l16_run[1]) + (l16_run[2] + l16_run[3]));
+    const float inv = 1.0f / l16_tot;
+    if (OUT_F32) {
+      if (wave_has_rows && qrow < p.Tq) {
+        const size_t orow = ((size_t)cur.bh * (size_t)p.Tq + (size_t)qrow) * D;
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-        m_run = m_new;
-        m_thr = m_new + kRescaleThreshold;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4_t f = {oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv,
+                               oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv};
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.o) + orow + 32 * db + 8 * i4 +
+                                        4 * g) = f;
+          }
       }
+    } else if (wave_has_rows) {
+      // In the MFMA layout a lane holds 8-byte pieces of one row; the rows go through this
+      // wave's 4 KB of LDS, 64 columns at a time (16-byte chunks XOR-swizzled by row), so that
+      // each global store writes whole 128-byte row segments.
+      const uint32_t ob = (uint32_t)reinterpret_cast<uintptr_t>(ostage) + (uint32_t)wave * 4096u;
+      const int rows = p.Tq - qw0;   // valid rows of this wave (>= 1)
+      uint16_t* const obase = static_cast<uint16_t*>(p.o) + ((size_t)cur.bh * p.Tq + qw0) * D;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int h = 0; h < ND / 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[kb][i], p.scale_log2, -m_run));
-          sacc[kb][i] = e;
-          l_run[i & 3] += e;
+        for (int db2 = 0; db2 < 2; ++db2)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x16_t& a = oacc[2 * h + db2];
+            const int ch = 4 * db2 + i4;   // columns 8*ch + 4*g .. + 3 of this half
+            lds_write8(ob + r32 * 128u + 16u * (ch ^ (r32 & 7)) + 8u * g,
+                       pack_bf16x4(a[4 * i4] * inv, a[4 * i4 + 1] * inv, a[4 * i4 + 2] * inv,
+                                   a[4 * i4 + 3] * inv));
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + (lane >> 3), ch = lane & 7;
+          const u32x4_t w = lds_read16u(ob + row * 128u + 16u * (ch ^ (row & 7)));
+          if (row < rows)
+            *reinterpret_cast<u32x4_t*>(obase + (size_t)row * D + 64 * h + 8 * ch) = w;
         }
-      // P^T as bf16 B operands: 16 keys per k-step, registers 8*(ks%2).. of score block ks/2
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f32x16_t& sb = sacc[ks >> 1];
-        const int b0 = (ks & 1) * 8;
-        const u32x2_t lo = pack_bf16x4(sb[b0], sb[b0 + 1], sb[b0 + 2], sb[b0 + 3]);
-        const u32x2_t hi = pack_bf16x4(sb[b0 + 4], sb[b0 + 5], sb[b0 + 6], sb[b0 + 7]);
-        u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-        pb[ks] = as_bf16x8(w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          l16_run[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[e]), ones_bf16x2(),
-                                                       l16_run[e], false);
       }
-      // the next section's leading operands: V^T of this tile
-#pragma unroll
-      for (int i = 0; i < PRE; ++i) ring[i] = v_opnd(v_at(t), i);
     }
+    if (wave_has_rows && qrow < p.Tq && g == 0)
+      p.lse[(size_t)cur.bh * p.Tq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
     __syncthreads();
-  };
-  // section 0's first operands: K of tile 0
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) ring[i] = k_opnd(k_at(0), i);
-  step(0, std::true_type{});
-  for (int t = 1; t <= ntiles; ++t) step(t, std::false_type{});
-  if (!group_b) __syncthreads();   // match group B's extra barrier
 
-  // ---- epilogue: O = acc / l16, LSE = (m + log2 l) * ln 2 ----
-  // (no LDS access: the next item's prologue may start filling stages right away)
-  const float l_tot = xhalf_sum((l_run[0] + l_run[1]) + (l_run[2] + l_run[3]));
-  const float l16_tot = xhalf_sum((l16_run[0] + l16_run[1]) + (l16_run[2] + l16_run[3]));
-  if (wave_has_rows && qrow < p.Tq) {
-  const float inv = 1.0f / l16_tot;
-  const size_t orow = qbase + (size_t)qrow * D;
-#pragma unroll
-  for (int db = 0; db < ND; ++db) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = 32 * db + 8 * i4 + 4 * g;
-      const float a0 = oacc[db][4 * i4 + 0] * inv, a1 = oacc[db][4 * i4 + 1] * inv;
-      const float a2 = oacc[db][4 * i4 + 2] * inv, a3 = oacc[db][4 * i4 + 3] * inv;
-      if (OUT_F32) {
-        f32x4_t f = {a0, a1, a2, a3};
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.o) + orow + d0) = f;
-      } else {
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.o) + orow + d0) =
-            pack_bf16x4(a0, a1, a2, a3);
-      }
-    }
+    g0 += ntiles;
+    cur = nxt;
   }
-  if (g == 0) p.lse[(size_t)bh * p.Tq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
-  }
-  }   // half
-  }   // pair
+  if (describe(c, 0).pp < PX && !group_b) __syncthreads();   // match group B's extra barrier
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
