@@ -109,6 +109,49 @@ def test_edge_shapes(gpu, B, h, Tq, Tk, d, causal):
                    heads)
 
 
+# Shapes with more (head, block-pair) items than CUs, so the kernel runs its persistent
+# schedule: head counts not divisible by the 8 XCD groups, odd block counts (a middle block with
+# no partner), causal with Tq < Tk, non-causal.
+PERSISTENT_SHAPES = [
+    (3, 37, 1100, 1100, 128, True), (3, 37, 1100, 1500, 64, True),
+    (2, 45, 1300, 1300, 128, False), (1, 130, 1024, 1024, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,h,Tq,Tk,d,causal", PERSISTENT_SHAPES)
+def test_persistent_schedule_shapes(gpu, B, h, Tq, Tk, d, causal):
+    wl = si.custom_workload(B, h, Tq, Tk, d, causal)
+    q, k, v = si.make_inputs(wl, seed=21, threads=8)
+    res = run_fwd(gpu, q, k, v, causal, wl.scale)
+    assert_bf16_is_rne_of_f32(res)
+    rng = np.random.default_rng(B * 1000 + h)
+    edge = np.array([0, 1, 255, 256, 511, 512, Tq // 2, Tq - 2, Tq - 1])
+    heads = {}
+    for bh in sorted({0, 1, 7, 8, 9, B * h // 2, B * h - 2, B * h - 1} |
+                     set(rng.choice(B * h, 8, replace=False).tolist())):
+        rows = np.unique(np.concatenate([edge, rng.choice(Tq, 24, replace=False)]))
+        heads[divmod(int(bh), h)] = rows
+    _check_sampled(f"persistent B{B} h{h} Tq{Tq} Tk{Tk} d{d} causal{int(causal)}", res, q, k, v,
+                   wl, heads)
+    # Every row of every item was written: its LSE lies between the row's largest visible score
+    # and that plus ln(#visible keys) (scores in fp32 on the CPU, a bound, not the oracle).
+    qf = torch.from_numpy(si.bf16_bits_to_f32(q)).reshape(B * h, Tq, d)
+    kf = torch.from_numpy(si.bf16_bits_to_f32(k)).reshape(B * h, Tk, d)
+    lse = res["lse32"].cpu().reshape(B * h, Tq)
+    cnt = torch.full((Tq,), float(Tk))
+    for i0 in range(0, B * h, 16):
+        sc = torch.bmm(qf[i0:i0 + 16], kf[i0:i0 + 16].transpose(1, 2).contiguous()) * wl.scale
+        if causal:
+            vis = torch.arange(Tk)[None, :] <= torch.arange(Tq)[:, None] + (Tk - Tq)
+            sc = sc.masked_fill(~vis, float("-inf"))
+            cnt = vis.sum(1).float()
+        mx = sc.amax(2)
+        part = lse[i0:i0 + 16]
+        assert torch.all(part >= mx - 1e-3), "an LSE below its row maximum: a row was not written"
+        assert torch.all(part <= mx + torch.log(cnt)[None] + 1e-3), "an LSE above its bound"
+    assert torch.isfinite(res["o32"]).all()
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_row_zero_is_exactly_first_value_row(gpu, d):
     wl = si.custom_workload(2, 4, 300, 300, d, True)
