@@ -43,3 +43,29 @@ def test_mutant_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
+
+
+BWD_SRC = os.path.join(ROOT, "oracle", "attention_bwd_ref.py")
+
+BWD_MUTANTS = {
+    "score gradient without D": ("dS = P * (dP - D[:, None])", "dS = P * dP"),
+    "score gradient sign flipped": ("dS = P * (dP - D[:, None])", "dS = P * (D[:, None] - dP)"),
+    "dQ without the scale": ("dq = float(scale) * (dS @ k)", "dq = (dS @ k)"),
+    "dK from dO instead of Q": ("dk = float(scale) * (dS.T @ q)", "dk = float(scale) * (dS.T @ do)"),
+    "dV from dS instead of P": ("dv = P.T @ do", "dv = dS.T @ do"),
+    "D from dP instead of O": ("D = np.sum(do * O, axis=1)", "D = np.sum(dP, axis=1) / Tk"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(BWD_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    path = tmp_path / "mutant_bwd.py"
+    path.write_text(src.replace(old, new))
+    env = dict(os.environ, FA_ORACLE_BWD_MUTANT_FILE=str(path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
