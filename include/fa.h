@@ -112,8 +112,53 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
               int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Host-only argument checks used by fa_fwd / fa_fwd_o32 and fa_decode (no HIP call is made).
- * Return FA_OK or the FA_ERR_* code the entry point would return. */
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd / fa_bwd_f32 need: two fp32 values
+ *   per query row (D_i and LSE_i * log2(e)), each array starting on a 256-byte boundary.
+ *   Returns 0 for sizes < 1.
+ */
+size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq);
+
+/*
+ * fa_bwd -- attention backward: the gradients of sum(dout * O) with respect to q, k and v,
+ *   where O, lse are fa_fwd's outputs for the same q, k, v, causal and scale.
+ *   q, o, dout [B][h][Tq][d_head] bf16; k, v [B][h][Tk][d_head] bf16; lse [B][h][Tq] fp32
+ *   (natural log, as fa_fwd writes it);
+ *   dq [B][h][Tq][d_head], dk, dv [B][h][Tk][d_head] bf16 (out).
+ *   The method is the recomputing backward of page "Chapter 10 Writing and Benchmarking Custom
+ *   Kernels", section 10.3.2: S = scale q k^T is recomputed tile by tile, P = exp(S - lse) is
+ *   rebuilt from the stored log-sum-exp, D_i = <dout_i, O_i>, dP = dout v^T and
+ *   dS = P (dP - D); then dv = P^T dout, dk = scale dS^T q, dq = scale dS k.  Nothing of size
+ *   Tq x Tk is stored.  Masking as in fa_fwd (causal: query i sees key j iff j <= i + Tk - Tq).
+ *   Precision: bf16 inputs, fp32 accumulation; P and dS are rounded to bf16 (round to nearest
+ *   even) as operands of the gradient products; outputs rounded to bf16.  The result is
+ *   deterministic (no atomics): the same inputs give the same bits.
+ *   Preconditions: as fa_fwd for sizes and alignment (all tensors 16-byte aligned, lse 4-byte);
+ *   workspace 16-byte aligned with workspace_bytes >= fa_bwd_workspace_size(B, h, Tq); the
+ *   outputs and the workspace must not overlap the inputs or each other.  Every element of dq,
+ *   dk and dv is written.  The workspace holds no state between calls.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head, int causal,
+           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_f32 -- the same computation and kernels with dq, dk, dv stored in fp32 (parity
+ *   diagnostics: fa_bwd's outputs are the round-to-nearest-even of these, bit for bit).
+ */
+int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, float* dq, float* dk, float* dv,
+               int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head, int causal,
+               float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode and fa_bwd / fa_bwd_f32
+ * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return. */
+int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, const void* dq, const void* dk,
+                    const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
+                    int64_t d_head, int causal, float scale, const void* workspace,
+                    size_t workspace_bytes);
 int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                     int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
                     int causal, float scale);

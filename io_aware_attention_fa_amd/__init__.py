@@ -1,4 +1,4 @@
-"""MI355X-native IO-aware attention: fused attention forward and split-KV decode.
+"""MI355X-native IO-aware attention: fused attention forward, split-KV decode and backward.
 
 A thin binding over the C ABI of ``include/fa.h`` (``libfa_mi355x.so``).  The functions carry the
 same names as the C entry points and only marshal arguments: torch supplies device memory and the
@@ -16,8 +16,9 @@ from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR
                    FA_ERR_NULL, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS, FA_ERR_WORKSPACE,
                    FA_OK, LIB_PATH)
 
-__all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_validate_fwd",
-           "fa_validate_decode", "fa_status_str", "fa_last_hip_error", "FaError", "LIB_PATH"]
+__all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
+           "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
+           "fa_validate_bwd", "fa_status_str", "fa_last_hip_error", "FaError", "LIB_PATH"]
 
 
 class FaError(RuntimeError):
@@ -41,6 +42,10 @@ def fa_last_hip_error() -> int:
 
 def fa_decode_workspace_size(B: int, h: int, d_head: int, num_splits: int) -> int:
     return int(_lib.lib.fa_decode_workspace_size(B, h, d_head, num_splits))
+
+
+def fa_bwd_workspace_size(B: int, h: int, Tq: int) -> int:
+    return int(_lib.lib.fa_bwd_workspace_size(B, h, Tq))
 
 
 def _check_tensor(name, t, dtype, ndim):
@@ -142,6 +147,73 @@ def fa_decode(q, k, v, *, num_splits: int, scale: float | None = None, o=None, l
     if st != FA_OK:
         raise FaError(st)
     return o, lse
+
+
+def _bwd(entry, out_dtype, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, stream):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    B, h, Tq, d = q.shape
+    Tk = k.shape[2]
+    if (tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d) or
+            tuple(o.shape) != (B, h, Tq, d) or tuple(do.shape) != (B, h, Tq, d)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, o {tuple(o.shape)}, do {tuple(do.shape)}")
+    _check_tensor("lse", lse, torch.float32, 3)
+    if tuple(lse.shape) != (B, h, Tq):
+        raise ValueError(f"lse must be [B, h, Tq], got {tuple(lse.shape)}")
+    if len({t.device for t in (q, k, v, o, do, lse)}) != 1:
+        raise ValueError("all inputs must be on the same device")
+    if dq is None:
+        dq = torch.empty((B, h, Tq, d), dtype=out_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, h, Tk, d), dtype=out_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, h, Tk, d), dtype=out_dtype, device=q.device)
+    for name, t, shape in (("dq", dq, (B, h, Tq, d)), ("dk", dk, (B, h, Tk, d)),
+                           ("dv", dv, (B, h, Tk, d))):
+        _check_tensor(name, t, out_dtype, 4)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    need = fa_bwd_workspace_size(B, h, Tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8, 1)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, Tq, Tk, d,
+               int(bool(causal)), scale, workspace.data_ptr(), workspace.numel(),
+               _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv
+
+
+def fa_bwd(q, k, v, o, do, lse, *, causal: bool, scale: float | None = None, dq=None, dk=None,
+           dv=None, workspace=None, stream=None):
+    """Attention backward -> (dq, dk, dv) bf16, the gradients of sum(do * o).
+
+    q, o, do [B,h,Tq,d] and k, v [B,h,Tk,d] bf16, lse [B,h,Tq] fp32: o and lse are
+    :func:`fa_fwd`'s outputs for the same q, k, v, causal and scale.  ``workspace`` (a uint8 GPU
+    tensor of at least fa_bwd_workspace_size bytes) and the outputs are allocated with
+    ``torch.empty`` unless given.
+    """
+    return _bwd(_lib.lib.fa_bwd, torch.bfloat16, q, k, v, o, do, lse, causal, scale, dq, dk, dv,
+                workspace, stream)
+
+
+def fa_bwd_f32(q, k, v, o, do, lse, *, causal: bool, scale: float | None = None, dq=None,
+               dk=None, dv=None, workspace=None, stream=None):
+    """Same kernels as :func:`fa_bwd` with fp32 gradients (parity diagnostics)."""
+    return _bwd(_lib.lib.fa_bwd_f32, torch.float32, q, k, v, o, do, lse, causal, scale, dq, dk,
+                dv, workspace, stream)
+
+
+def fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, B, h, Tq,
+                    Tk, d_head, causal, scale, ws_ptr, ws_bytes):
+    """Host-only argument check of the backward entry points (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr,
+                                        dk_ptr, dv_ptr, B, h, Tq, Tk, d_head, int(causal),
+                                        float(scale), ws_ptr, ws_bytes))
 
 
 def fa_validate_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head, causal, scale):

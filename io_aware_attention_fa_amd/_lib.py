@@ -29,6 +29,13 @@ SIGNATURES = {
     "fa_validate_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _f32]),
     "fa_validate_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64,
                                   _vp, _size]),
+    "fa_bwd_workspace_size": (_size, [_i64, _i64, _i64]),
+    "fa_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                      _int, _f32, _vp, _size, _vp]),
+    "fa_bwd_f32": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                          _i64, _int, _f32, _vp, _size, _vp]),
+    "fa_validate_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                               _i64, _i64, _int, _f32, _vp, _size]),
     "fa_status_str": (ctypes.c_char_p, [_int]),
     "fa_last_hip_error": (_int, []),
 }

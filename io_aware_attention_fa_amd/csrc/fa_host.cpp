@@ -54,4 +54,43 @@ extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, f
   return map_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t h, int64_t Tq,
+               int64_t Tk, int64_t d, int causal, float scale, void* workspace,
+               size_t workspace_bytes, void* stream, bool out_f32) {
+  const int st = fa_validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d, causal, scale,
+                                 workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::BwdLaunch a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  // the workspace holds two arrays of B*h*Tq floats, the second on a 256-byte boundary
+  const size_t half = fa_bwd_workspace_size(B, h, Tq) / 2;
+  a.l2 = static_cast<float*>(workspace);
+  a.dd = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
+  a.B = static_cast<int>(B); a.H = static_cast<int>(h);
+  a.Tq = static_cast<int>(Tq); a.Tk = static_cast<int>(Tk); a.d = static_cast<int>(d);
+  a.causal = causal != 0; a.out_f32 = out_f32; a.scale = scale;
+  return map_hip(fa::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head, int causal,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d_head, causal, scale,
+                    workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                          int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                          int causal, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d_head, causal, scale,
+                    workspace, workspace_bytes, stream, true);
+}
+
 extern "C" int fa_last_hip_error(void) { return g_last_hip_error; }

@@ -29,7 +29,26 @@ struct DecodeLaunch {
   float scale;
 };
 
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* l2;   // workspace: LSE * log2(e) per query row
+  float* dd;   // workspace: D_i = <dO_i, O_i> per query row
+  int B, H, Tq, Tk, d;
+  bool causal;
+  bool out_f32;
+  float scale;
+};
+
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);
 
 }  // namespace fa

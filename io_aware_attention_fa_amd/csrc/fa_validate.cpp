@@ -66,6 +66,43 @@ extern "C" int fa_validate_decode(const void* q, const void* k, const void* v, c
   return FA_OK;
 }
 
+namespace {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+extern "C" size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq) {
+  if (B < 1 || h < 1 || Tq < 1) return 0;
+  return 2 * round256(static_cast<size_t>(B) * static_cast<size_t>(h) * static_cast<size_t>(Tq) *
+                      sizeof(float));
+}
+
+extern "C" int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, const void* dq, const void* dk,
+                               const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
+                               int64_t d_head, int causal, float scale, const void* workspace,
+                               size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_bytes_ok(Tq, d_head) || !head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
+  // grids: one workgroup per (128-row block, head); the preprocess takes >= 16 rows per
+  // workgroup and indexes rows in 64 bits
+  const int64_t nb = ((Tq > Tk ? Tq : Tk) + 127) / 128;
+  if (B > INT32_MAX / h || B * h > INT32_MAX / nb) return FA_ERR_SHAPE;
+  if (B * h > (int64_t)UINT32_MAX * 16 / Tq) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Tq > Tk) return FA_ERR_CAUSAL_TQ_GT_TK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < fa_bwd_workspace_size(B, h, Tq))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

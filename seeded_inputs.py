@@ -7,7 +7,8 @@ bfloat16, so that both sides consume the very same bf16 bits.
 Generator (fixed so that any single head can be regenerated on its own):
   * every (tensor, batch b, head h) slice is drawn from numpy's PCG64 stream
     ``default_rng([seed, tensor_id, b, h])`` with ``standard_normal(dtype=float32)``, in row-major
-    [T][d] order; tensor ids are Q=0, K=1, V=2 and the key-spike mask stream is 3;
+    [T][d] order; tensor ids are Q=0, K=1, V=2, the key-spike mask stream is 3 and the output
+    gradient dO of the backward workloads is 4 (standard normal like the others);
   * float32 -> bfloat16 is round-to-nearest-even on the bit pattern (inputs are finite);
   * the long-context workload scales a Bernoulli(1%) subset of key vectors by 8 (a power of two,
     so the scaling is exact in bf16); the subset of head (b, h) is ``random(T) < 0.01`` drawn from
@@ -24,7 +25,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_KEY_SPIKES = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_KEY_SPIKES, TENSOR_DO = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -131,6 +132,19 @@ def make_inputs(wl: Workload, seed: int = 0, threads: int | None = None):
     if wl.decode:
         q = q.reshape(wl.B, wl.h, wl.d)
     return q, k, v
+
+
+def make_grad(wl: Workload, seed: int = 0, threads: int | None = None) -> np.ndarray:
+    """The output gradient dO [B][h][Tq][d] (bf16 bits) of a backward workload."""
+    do = np.empty((wl.B, wl.h, wl.Tq, wl.d), dtype=np.uint16)
+
+    def fill(bh):
+        b, h = divmod(bh, wl.h)
+        do[b, h] = head_normal_bits(seed, TENSOR_DO, b, h, wl.Tq, wl.d)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(fill, range(wl.B * wl.h)))
+    return do
 
 
 def custom_workload(B, h, Tq, Tk, d, causal, name="custom", **kw) -> Workload:

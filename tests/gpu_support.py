@@ -75,3 +75,90 @@ def assert_bf16_is_rne_of_f32(res):
     assert torch.equal(o16.view(torch.int16), rne_bf16_of(o32).view(torch.int16)), \
         "bf16 output is not the round-to-nearest-even of the fp32 output"
     assert torch.equal(res["lse16"], res["lse32"])
+
+
+# ---- backward ----------------------------------------------------------------------------------
+# Tolerance of a backward gradient element, derived from the kernels' arithmetic: P and dS are
+# rounded to bf16 (unit roundoff u = 2^-8) as MFMA operands, the gradients are accumulated in fp32
+# (at most a few thousand terms: < 2^-11 relative to the sum of absolute products A), and the
+# bf16 outputs add one more rounding (<= u |x| <= u A).  So |gpu - exact| <= FAC * A with
+# FAC = 2u + 2^-11 (bf16 outputs) or u + 2^-11 (fp32 outputs), plus the error that reaches dS
+# through D_i = <dO_i, O_i> when O is given in bf16 (|dD_i| <= u_O sum_d |dO_id| |O_id|) and
+# the fp32 rounding of dP - D (<= 2^-16 (sum_d |dO_id V_jd| + |D_i|)).
+BWD_FAC_BF16 = 2.0 ** -7 + 2.0 ** -11
+BWD_FAC_F32 = 2.0 ** -8 + 2.0 ** -11
+
+
+def bwd_tolerances(r, q, k, v, do, scale, fac, o_err=None):
+    """Per-element tolerances {dq, dk, dv} for one head from the oracle's intermediates r.
+
+    ``o_err`` [Tq][d] bounds |O_given - O_exact| (default: bf16 rounding of the exact O)."""
+    from oracle import attention_bwd_ref as bref
+    A = bref.abs_bounds_head(r, q, k, do, scale)
+    if o_err is None:
+        o_err = 2.0 ** -8 * np.abs(r["O"])
+    ado = np.abs(do)
+    dD = np.sum(ado * o_err, axis=1)                          # |dD_i|
+    E = np.sum(ado * np.abs(r["O"]), axis=1)                  # sum of |terms| of D_i
+    G = ado @ np.abs(v).T + E[:, None]                        # magnitudes in dP - D
+    err_ds = r["P"] * (dD[:, None] + 2.0 ** -16 * G)          # |error of dS_ij| beyond rounding
+    s = abs(float(scale))
+    return {"dq": fac * A["dq"] + s * (err_ds @ np.abs(k)) + 1e-7,
+            "dk": fac * A["dk"] + s * (err_ds.T @ np.abs(q)) + 1e-7,
+            "dv": fac * A["dv"] + 1e-7}
+
+
+def oracle_bwd_head(q_bits, k_bits, v_bits, do_bits, scale, causal):
+    """fp64 oracle backward of one head from bf16 bits, plus the O (bf16 bits, RNE) and LSE (fp32)
+    the kernels take as inputs."""
+    from oracle import attention_bwd_ref as bref
+    q, k, v, do = (si.bf16_bits_to_f64(x) for x in (q_bits, k_bits, v_bits, do_bits))
+    r = bref.backward_head(q, k, v, do, scale, causal)
+    o_bits = si.rne_bf16_bits(r["O"].astype(np.float32))
+    return r, (q, k, v, do), o_bits, r["LSE"].astype(np.float32)
+
+
+def run_bwd(fa, q, k, v, o, do, lse, causal, scale, f32=True):
+    """GPU backward through the C ABI; q, k, v, o, do bf16 bits, lse fp32 (numpy or torch)."""
+    qg, kg, vg, og, dog = (x if isinstance(x, torch.Tensor) else to_gpu(x)
+                           for x in (q, k, v, o, do))
+    lg = lse if isinstance(lse, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(lse)).cuda()
+    res = {}
+    res["dq16"], res["dk16"], res["dv16"] = fa.fa_bwd(qg, kg, vg, og, dog, lg, causal=causal,
+                                                      scale=scale)
+    if f32:
+        res["dq32"], res["dk32"], res["dv32"] = fa.fa_bwd_f32(qg, kg, vg, og, dog, lg,
+                                                              causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_bwd_head(tag, res, bh, r, x64, scale, o_err=None):
+    """Gate one head's gradients (fp32 and bf16 outputs) against the oracle."""
+    q, k, v, do = x64
+    b, h = bh
+    worst = {}
+    for out, fac in (("32", BWD_FAC_F32), ("16", BWD_FAC_BF16)):
+        if "dq" + out not in res:
+            continue
+        tol = bwd_tolerances(r, q, k, v, do, scale, fac, o_err)
+        for name in ("dq", "dk", "dv"):
+            got = res[name + out][b, h].float().cpu().numpy().astype(np.float64)
+            err = np.abs(got - r[name])
+            ratio = float(np.max(err / tol[name])) if err.size else 0.0
+            worst[name + out] = (float(np.max(err)), ratio)
+            assert np.all(np.isfinite(got)), f"{tag} {name}{out}: non-finite output"
+            bad = np.argwhere(err > tol[name])
+            assert bad.size == 0, (f"{tag} {name}{out}: {len(bad)} elements beyond tolerance, "
+                                   f"first {tuple(bad[0])} err {err[tuple(bad[0])]:.3e} "
+                                   f"tol {tol[name][tuple(bad[0])]:.3e}")
+    log(f"[parity] {tag} head {bh}: " +
+        " ".join(f"{k}: max|d|={a:.2e} (x{rr:.3f} of tol)" for k, (a, rr) in worst.items()))
+    return worst
+
+
+def assert_bwd_bf16_is_rne_of_f32(res):
+    for name in ("dq", "dk", "dv"):
+        assert torch.equal(res[name + "16"].view(torch.int16),
+                           rne_bf16_of(res[name + "32"]).view(torch.int16)), \
+            f"bf16 {name} is not the round-to-nearest-even of the fp32 {name}"

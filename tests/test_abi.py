@@ -120,3 +120,52 @@ def test_invalid_calls_touch_nothing(fa_lib):
                             ws.nbytes, None)
     assert st == 7
     assert np.all(o == 0x7FC1) and np.all(lse == 12345.0) and np.all(ws == 7)
+
+
+def test_bwd_workspace_size(fa_lib):
+    n = 2 * 3 * 100 * 4
+    assert fa_lib.fa_bwd_workspace_size(2, 3, 100) == 2 * ((n + 255) // 256 * 256)
+    assert fa_lib.fa_bwd_workspace_size(0, 3, 100) == 0
+    assert fa_lib.fa_bwd_workspace_size(1, 1, 64) == 512
+
+
+def _vb(fa_lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, h=2, Tq=100, Tk=120, d=128,
+             causal=1, scale=0.1, ws=P, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = fa_lib.fa_bwd_workspace_size(max(a["B"], 1), max(a["h"], 1),
+                                                     max(a["Tq"], 1))
+    return fa_lib.fa_validate_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                  a["dk"], a["dv"], a["B"], a["h"], a["Tq"], a["Tk"], a["d"],
+                                  a["causal"], a["scale"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"do": 0}, 1), ({"dv": 0}, 1), ({"lse": 0}, 1),
+    ({"Tq": 0}, 2), ({"B": 0}, 2), ({"Tk": 2**30}, 2),
+    ({"d": 80}, 3),
+    ({"Tq": 121}, 4), ({"Tq": 121, "causal": 0}, 0),
+    ({"do": P + 8}, 5), ({"dk": P + 2}, 5), ({"lse": P + 2}, 5),
+    ({"scale": math.nan}, 6), ({"causal": 3}, 6),
+    ({"ws": 0}, 8), ({"ws": P + 4}, 8), ({"ws_bytes": 100}, 8),
+])
+def test_validate_bwd(fa_lib, kw, code):
+    assert _vb(fa_lib, **kw) == code
+
+
+def test_invalid_bwd_call_touches_nothing(fa_lib):
+    from io_aware_attention_fa_amd import _lib
+    buf = np.zeros(4096, dtype=np.uint16)
+    out = np.full(4096, 0x7FC1, dtype=np.uint16)
+    lse = np.zeros(64, dtype=np.float32)
+    ws = np.full(4096, 7, dtype=np.uint8)
+    a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, buf, buf, lse, out, out, out)]
+    st = _lib.lib.fa_bwd(*a, 1, 1, 16, 16, 96, 0, 0.125, ctypes.c_void_p(ws.ctypes.data),
+                         ws.nbytes, None)
+    assert st == 3
+    st = _lib.lib.fa_bwd_f32(*a, 1, 1, 17, 16, 64, 1, 0.125, ctypes.c_void_p(ws.ctypes.data),
+                             ws.nbytes, None)
+    assert st == 4
+    assert np.all(out == 0x7FC1) and np.all(ws == 7)
