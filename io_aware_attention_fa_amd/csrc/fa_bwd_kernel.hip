@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 #include "fa_lds.hpp"
@@ -181,6 +183,67 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------------------
+// Software pipeline of the two gradient kernels.  The work on one streamed tile has three parts:
+//   A: the score-side products (S and dP) of the tile, from row operands in LDS;
+//   V: the elementwise part, P = exp2(S * scale * log2 e - L2), dS = P (dP - D), rounded to bf16;
+//   C: the gradient products that consume P and dS, from transposed operands in LDS.
+// Step s runs C of tile s - 1 with V of tile s scheduled between its MFMAs (one wave per SIMD:
+// the vector instructions issue while the matrix core works), then A of tile s + 1.  V of tile s
+// reads the score registers A filled in the previous step and writes the bf16 operands of the
+// next step's C, which are handed over by register moves at the end of the step.  Every MFMA
+// operand streams from LDS through a ring of kRing registers, each read issued kRing MFMAs ahead
+// of its use.  Tiles go through a 4-stage LDS ring: at step s, tile s + 2 is requested into the
+// stage tile s - 2 left (its last use, C of step s - 1, is behind the barrier that ended that
+// step), and the step ends once it has landed.
+constexpr int kRing = 8;
+
+// A step's MFMA stream: NC C-part MFMAs (two transposing reads each), then NA A-part MFMAs (one
+// LDS read each); VPM vector instructions are scheduled after each C-part MFMA (after each
+// A-part MFMA when there is no C part), and the step issues XR extra LDS reads up front.
+template <int NC, int NA, int VPM, int XR>
+struct StepSeq {
+  static constexpr int n = NC + NA;
+  static constexpr __device__ int reads(int i) { return i < NC ? 2 : 1; }
+  static constexpr __device__ int valu(int i) { return (NC > 0 ? i < NC : i < NA) ? VPM : 0; }
+  static constexpr __device__ int initial_reads() {
+    int r = XR;
+    for (int i = 0; i < kRing && i < n; ++i) r += reads(i);
+    return r;
+  }
+};
+
+template <class S, int I>
+__device__ __forceinline__ void sched_step() {
+  if constexpr (I < S::n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA I
+    if constexpr (I + kRing < S::n)
+      __builtin_amdgcn_sched_group_barrier(0x100, S::reads(I + kRing), 0);   // its ring refill
+    if constexpr (S::valu(I) > 0) __builtin_amdgcn_sched_group_barrier(0x002, S::valu(I), 0);
+    sched_step<S, I + 1>();
+  }
+}
+template <class S>
+__device__ __forceinline__ void sched_pattern() {
+  if constexpr (S::initial_reads() > 0)
+    __builtin_amdgcn_sched_group_barrier(0x100, S::initial_reads(), 0);
+  sched_step<S, 0>();
+}
+
+// Packs registers 8*(ks%2) .. +7 of a 16-register MFMA result block into one bf16 B operand
+// (RNE): the 16 streamed rows of k-step ks.
+__device__ __forceinline__ bf16x8_t pack_kstep(const f32x16_t& x, int half) {
+  const int b0 = 8 * half;
+  const u32x2_t lo = pack_bf16x4(x[b0], x[b0 + 1], x[b0 + 2], x[b0 + 3]);
+  const u32x2_t hi = pack_bf16x4(x[b0 + 4], x[b0 + 5], x[b0 + 6], x[b0 + 7]);
+  return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+
+template <bool C, bool V, bool A, bool M>
+struct Parts {
+  static constexpr bool c = C, v = V, a = A, m = M;
+};
+
+// ---------------------------------------------------------------------------------------------
 // dK, dV: one workgroup per (128-key block, head), lane = key.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -188,7 +251,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   using T = BTile<D>;
   constexpr int NS = D / 16;   // k-steps over d
   constexpr int ND = D / 32;   // 32-row blocks of dK^T / dV^T
-  // LDS: Q stages, dO stages, then 64 floats of L and of D per stage.
+  constexpr int NA = 4 * NS;   // S and dP MFMAs per tile
+  constexpr int NC = 8 * ND;   // dV^T and dK^T MFMAs per tile
+  // LDS: Q stages, dO stages, then 64 floats of L2 and of D per stage.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
   __shared__ __attribute__((aligned(256))) float lds_ld[2 * kStages * kRows];
   const uint32_t lq = (uint32_t)reinterpret_cast<uintptr_t>(lds);
@@ -206,6 +271,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
   const int kw0 = blk * kOwn + wave * 32;   // this wave's first key
   const int key = kw0 + r32;
+  // P is zeroed for queries below thr: keys past the end see nothing; causal keys see queries
+  // from key - off on
+  const int thr = key >= p.Tk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
 
   // K and V rows of this lane's key as B operands (k = 8 columns per lane half).
   bf16x8_t kf[NS], vf[NS];
@@ -240,12 +308,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
       lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
     }
-    // every wave writes the same 64 values of L and D (identical data, so the copies agree)
+    // every wave writes the same 64 values of L2 and D (identical data, so the copies agree)
     const uint32_t r0 = (uint32_t)((t0 + it) * kRows + lane) * 4u;
     lds_dma4(rl, ll + st * (kRows * 4), r0);
     lds_dma4(rd, ld + st * (kRows * 4), r0);
   };
-  constexpr int kVmcntTile = vmcnt_imm(2 * T::LPW + 2);
 
   f32x16_t accv[ND], acck[ND];
 #pragma unroll
@@ -253,89 +320,105 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     accv[db] = f32x16_t{};
     acck[db] = f32x16_t{};
   }
+  f32x16_t sacc[2], dpacc[2];   // [32-query block]: S then P, dP then dS
+  bf16x8_t pb[4], dsb[4];       // P and dS of the previous tile (C operands)
+  bf16x8_t ring[kRing];
 
-  request(0);
-  if (nt > 1) request(1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    const int st = it & (kStages - 1);
-    if (it + 2 < nt) request(it + 2);
-    const int qt0 = (t0 + it) * kRows;
-    // a wave whose keys all lie after this tile's last query (+ off) has nothing to do
-    const bool active = !(CAUSAL && kw0 > qt0 + kRows - 1 + off);
-    if (active) {
-      const uint32_t aq = lq + st * T::BYTES, ado = ldo + st * T::BYTES;
-      // ---- S = Q K^T and dP = dO V^T: rows = 64 queries (two 32-row blocks), column = key
-      f32x16_t s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
+  // Step s (see the pipeline above).  In the MFMA result layout, register i of 32-query block
+  // qb holds query 64*(t0 + s) + 32*qb + 8*(i/4) + 4*g + i%4 for key `key`.
+  auto step = [&](auto parts, const int s) {
+    using PT = decltype(parts);
+    constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+    using S = StepSeq<nc, na, PT::v ? 7 : 0, PT::v ? 16 : 0>;
+    if (s + 2 < nt) request(s + 2);
+    const uint32_t qc = lq + ((s - 1) & 3) * T::BYTES + ln.tr_off;
+    const uint32_t doc = ldo + ((s - 1) & 3) * T::BYTES + ln.tr_off;
+    const uint32_t qa = lq + ((s + 1) & 3) * T::BYTES + ln.row_off;
+    const uint32_t doa = ldo + ((s + 1) & 3) * T::BYTES + ln.row_off;
+    auto opnd = [&](int i) -> bf16x8_t {
+      if (i < nc) {
+        const int r = i % (2 * ND);
+        return tr_opnd<D>((r & 1) ? qc : doc, r >> 1, i / (2 * ND));
+      }
+      const int j = i - nc;
+      return row_opnd<D>((j & 1) ? doa : qa, (j >> 1) & 1, j >> 2);
+    };
 #pragma unroll
-      for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = mfma_32x32x16(row_opnd<D>(aq + ln.row_off, qb, ss), kf[ss], s[qb]);
-          dp[qb] = mfma_32x32x16(row_opnd<D>(ado + ln.row_off, qb, ss), vf[ss], dp[qb]);
-        }
-      // ---- P = exp2(S * scale * log2 e - L2), dS = P (dP - D); register i of block qb is
-      //      query qt0 + 32*qb + 8*(i/4) + 4*g + i%4
-      const bool need_mask =
-          (kw0 + 31 >= p.Tk) || (CAUSAL && kw0 + 31 > qt0 + off);
-      const uint32_t lls = ll + st * (kRows * 4), lds_s = ld + st * (kRows * 4);
+    for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+    bf16x8_t pn[4], dsn[4];
+    if constexpr (PT::v) {
+      const uint32_t lo = ll + (s & 3) * (kRows * 4), dof = ld + (s & 3) * (kRows * 4);
+      f32x4_t L4[2][4], D4[2][4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const uint32_t o4 = 4u * (uint32_t)(32 * qb + 8 * a + 4 * g);
-          const f32x4_t L4 = lds_read_f32x4(lls + o4);
-          const f32x4_t D4 = lds_read_f32x4(lds_s + o4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * a + e;
-            float pv = fast_exp2(__builtin_fmaf(s[qb][i], p.c, -L4[e]));
-            if (need_mask) {
-              const int qi = qt0 + 32 * qb + 8 * a + 4 * g + e;
-              if (key >= p.Tk || (CAUSAL && key > qi + off)) pv = 0.f;
-            }
-            s[qb][i] = pv;
-            dp[qb][i] = pv * (dp[qb][i] - D4[e]);
-          }
+          L4[qb][a] = lds_read_f32x4(lo + o4);
+          D4[qb][a] = lds_read_f32x4(dof + o4);
         }
-      // B operands for 16-query k-step ks: registers 8*(ks%2) .. +7 of block ks/2
-      bf16x8_t pb[4], dsb[4];
+      const int q0 = (t0 + s) * kRows + 4 * g;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int a = i >> 2, e = i & 3;
+          float pv = fast_exp2(__builtin_fmaf(sacc[qb][i], p.c, -L4[qb][a][e]));
+          if (q0 + 32 * qb + 8 * a + e < thr) pv = 0.f;
+          sacc[qb][i] = pv;
+          dpacc[qb][i] = pv * (dpacc[qb][i] - D4[qb][a][e]);
+        }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int qb = ks >> 1, b0 = (ks & 1) * 8;
-        {
-          const u32x2_t lo = pack_bf16x4(s[qb][b0], s[qb][b0 + 1], s[qb][b0 + 2], s[qb][b0 + 3]);
-          const u32x2_t hi =
-              pack_bf16x4(s[qb][b0 + 4], s[qb][b0 + 5], s[qb][b0 + 6], s[qb][b0 + 7]);
-          pb[ks] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-        }
-        {
-          const u32x2_t lo =
-              pack_bf16x4(dp[qb][b0], dp[qb][b0 + 1], dp[qb][b0 + 2], dp[qb][b0 + 3]);
-          const u32x2_t hi =
-              pack_bf16x4(dp[qb][b0 + 4], dp[qb][b0 + 5], dp[qb][b0 + 6], dp[qb][b0 + 7]);
-          dsb[ks] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-        }
+        pn[ks] = pack_kstep(sacc[ks >> 1], ks & 1);
+        dsn[ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
       }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (rows = d, column = key)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          accv[db] = mfma_32x32x16(tr_opnd<D>(ado + ln.tr_off, db, ks), pb[ks], accv[db]);
-          acck[db] = mfma_32x32x16(tr_opnd<D>(aq + ln.tr_off, db, ks), dsb[ks], acck[db]);
-        }
     }
-    // tile it + 1 has landed (this wave's part); tile it + 2 may still be in flight
-    if (it + 2 < nt)
-      __builtin_amdgcn_s_waitcnt(kVmcntTile);
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int i = 0; i < S::n; ++i) {
+      const bf16x8_t a = ring[i % kRing];
+      if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+      if (i < nc) {
+        const int r = i % (2 * ND), ks = i / (2 * ND);
+        if (r & 1)
+          acck[r >> 1] = mfma_32x32x16(a, dsb[ks], acck[r >> 1]);
+        else
+          accv[r >> 1] = mfma_32x32x16(a, pb[ks], accv[r >> 1]);
+      } else {
+        const int j = i - nc, ss = j >> 2, qb = (j >> 1) & 1;
+        const bool first = ss == 0;
+        if (j & 1)
+          dpacc[qb] = mfma_32x32x16(a, vf[ss], first ? f32x16_t{} : dpacc[qb]);
+        else
+          sacc[qb] = mfma_32x32x16(a, kf[ss], first ? f32x16_t{} : sacc[qb]);
+      }
+    }
+    sched_pattern<S>();
+    if constexpr (PT::v) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        pb[ks] = pn[ks];
+        dsb[ks] = dsn[ks];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile s + 2 has landed (this wave's part)
     __syncthreads();
+  };
+
+  request(0);
+  if (nt > 1) request(1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  // steps -1 .. nt: A of tile 0; then C of s - 1, V of s, A of s + 1; then the last C
+  step(Parts<false, false, true, false>{}, -1);
+  if (nt > 1) {
+    step(Parts<false, true, true, false>{}, 0);
+    for (int s = 1; s + 1 < nt; ++s) step(Parts<true, true, true, false>{}, s);
+    step(Parts<true, true, false, false>{}, nt - 1);
+  } else {
+    step(Parts<false, true, false, false>{}, 0);
   }
+  step(Parts<true, false, false, false>{}, nt);
 
   // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
   if (key < p.Tk) {
@@ -361,6 +444,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
   using T = BTile<D>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
+  constexpr int NA = 4 * NS;   // S^T and dP^T MFMAs per tile
+  constexpr int NC = 4 * ND;   // dQ^T MFMAs per tile
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t lv = lk + kStages * T::BYTES;
@@ -376,8 +461,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int i0 = blk * kOwn;
   const int qw0 = i0 + wave * 32;
   const int qrow = qw0 + r32;
-  const int qw_last = min(qw0 + 31, p.Tq - 1);
-  const bool wave_has_rows = qw0 < p.Tq;
+  // keys above lim get P = 0 (past the end, or above the diagonal)
+  const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
 
   // Q and dO rows of this lane's query as B operands, and its L2 and D.
   bf16x8_t qf[NS], dof[NS];
@@ -414,73 +499,91 @@ void fa_bwd_dq_kernel(BwdParams p) {
       lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
     }
   };
-  constexpr int kVmcntTile = vmcnt_imm(2 * T::LPW);
 
   f32x16_t accq[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) accq[db] = f32x16_t{};
+  f32x16_t sacc[2], dpacc[2];   // [32-key block]: S^T, dP^T (then dS^T)
+  bf16x8_t dsb[4], ring[kRing];
+
+  // Step s.  Register i of 32-key block kb holds key 64*s + 32*kb + 8*(i/4) + 4*g + i%4 for
+  // query `qrow`.
+  auto step = [&](auto parts, const int s) {
+    using PT = decltype(parts);
+    constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+    using S = StepSeq<nc, na, PT::v ? (PT::m ? 12 : 8) : 0, 0>;
+    if (s + 2 < nt) request(s + 2);
+    const uint32_t kc = lk + ((s - 1) & 3) * T::BYTES + ln.tr_off;
+    const uint32_t ka = lk + ((s + 1) & 3) * T::BYTES + ln.row_off;
+    const uint32_t va = lv + ((s + 1) & 3) * T::BYTES + ln.row_off;
+    auto opnd = [&](int i) -> bf16x8_t {
+      if (i < nc) return tr_opnd<D>(kc, i % ND, i / ND);
+      const int j = i - nc;
+      return row_opnd<D>((j & 1) ? va : ka, (j >> 1) & 1, j >> 2);
+    };
+#pragma unroll
+    for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+    bf16x8_t dsn[4];
+    if constexpr (PT::v) {
+      const int kj0 = s * kRows + 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
+          if (PT::m && kj0 + 32 * kb + 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
+          dpacc[kb][i] = pv * (dpacc[kb][i] - dq_d);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dsn[ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+    }
+#pragma unroll
+    for (int i = 0; i < S::n; ++i) {
+      const bf16x8_t a = ring[i % kRing];
+      if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+      if (i < nc) {
+        accq[i % ND] = mfma_32x32x16(a, dsb[i / ND], accq[i % ND]);
+      } else {
+        const int j = i - nc, ss = j >> 2, kb = (j >> 1) & 1;
+        const bool first = ss == 0;
+        if (j & 1)
+          dpacc[kb] = mfma_32x32x16(a, dof[ss], first ? f32x16_t{} : dpacc[kb]);
+        else
+          sacc[kb] = mfma_32x32x16(a, qf[ss], first ? f32x16_t{} : sacc[kb]);
+      }
+    }
+    sched_pattern<S>();
+    if constexpr (PT::v) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dsb[ks] = dsn[ks];
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+  };
+  // tile s needs masking for this wave if a key is past the end or above a query's diagonal
+  auto need_mask = [&](int s) {
+    return (s * kRows + kRows > p.Tk) || (CAUSAL && s * kRows + kRows - 1 > qw0 + off);
+  };
 
   request(0);
   if (nt > 1) request(1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    const int st = it & (kStages - 1);
-    if (it + 2 < nt) request(it + 2);
-    const int j0 = it * kRows;
-    const bool active = wave_has_rows && !(CAUSAL && j0 > qw_last + off);
-    if (active) {
-      const uint32_t ak = lk + st * T::BYTES, av = lv + st * T::BYTES;
-      // ---- S^T = K Q^T and dP^T = V dO^T: rows = 64 keys (two 32-row blocks), column = query
-      f32x16_t s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = f32x16_t{};
-#pragma unroll
-      for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = mfma_32x32x16(row_opnd<D>(ak + ln.row_off, kb, ss), qf[ss], s[kb]);
-          dp[kb] = mfma_32x32x16(row_opnd<D>(av + ln.row_off, kb, ss), dof[ss], dp[kb]);
-        }
-      // ---- P^T and dS^T; register i of block kb is key j0 + 32*kb + 8*(i/4) + 4*g + i%4
-      const bool need_mask = (j0 + kRows > p.Tk) || (CAUSAL && j0 + kRows - 1 > qw0 + off);
-      const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(__builtin_fmaf(s[kb][i], p.c, -l2q));
-          if (need_mask) {
-            const int kj = j0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (kj > lim) pv = 0.f;
-          }
-          dp[kb][i] = pv * (dp[kb][i] - dq_d);
-        }
-      bf16x8_t dsb[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, b0 = (ks & 1) * 8;
-        const u32x2_t lo =
-            pack_bf16x4(dp[kb][b0], dp[kb][b0 + 1], dp[kb][b0 + 2], dp[kb][b0 + 3]);
-        const u32x2_t hi =
-            pack_bf16x4(dp[kb][b0 + 4], dp[kb][b0 + 5], dp[kb][b0 + 6], dp[kb][b0 + 7]);
-        dsb[ks] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-      }
-      // ---- dQ^T += K^T dS^T (rows = d, column = query)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-          accq[db] = mfma_32x32x16(tr_opnd<D>(ak + ln.tr_off, db, ks), dsb[ks], accq[db]);
+  step(Parts<false, false, true, false>{}, -1);
+  if (nt > 1) {
+    if (need_mask(0)) step(Parts<false, true, true, true>{}, 0);
+    else step(Parts<false, true, true, false>{}, 0);
+    for (int s = 1; s + 1 < nt; ++s) {
+      if (need_mask(s)) step(Parts<true, true, true, true>{}, s);
+      else step(Parts<true, true, true, false>{}, s);
     }
-    if (it + 2 < nt)
-      __builtin_amdgcn_s_waitcnt(kVmcntTile);
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    step(Parts<true, true, false, true>{}, nt - 1);
+  } else {
+    step(Parts<false, true, false, true>{}, 0);
   }
+  step(Parts<true, false, false, false>{}, nt);
 
-  if (wave_has_rows && qrow < p.Tq) {
+  if (qrow < p.Tq) {
     const size_t row = ((size_t)bh * (size_t)p.Tq + (size_t)qrow) * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
