@@ -11,6 +11,9 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
   roofline = that kernel against the MI355X dense-bf16 MFMA peak
   decode   = decode HBM GB/s (K+V bytes / average decode duration) against the HBM peak
   cpu_baseline = the fp64 CPU oracle timed on a bounded sample of the same forward workload
+  backward = the attention backward (dQ, dK, dV) on the forward workload, timed separately
+             after the steps (not part of ms_per_step): TFLOP/s at 2.5x the forward's FLOPs,
+             against the MFMA peak, with its own bounded CPU-oracle sample
 """
 from __future__ import annotations
 
@@ -95,14 +98,95 @@ def cpu_baseline(seconds_budget: float):
                       f"{elapsed:.1f} s of fp64 numpy; FLOPs counted as 4*T*T*d/2 per head"}
 
 
+def cpu_baseline_backward(seconds_budget: float):
+    """Time the fp64 backward oracle on whole heads of the forward workload (bounded sample)."""
+    import numpy as np  # noqa: F401
+    import seeded_inputs as si
+    from io_aware_attention_fa_amd import costmodel as cm
+    from oracle import attention_bwd_ref as bref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = si.WORKLOADS[PREFILL]
+    heads, elapsed = 0, 0.0
+    while heads == 0 or (elapsed < seconds_budget and heads < wl.B * wl.h):
+        b, h = divmod(heads, wl.h)
+        q, k, v = si.head_inputs(wl, 0, b, h)
+        do = si.head_normal_bits(0, si.TENSOR_DO, b, h, wl.Tq, wl.d)
+        q, k, v, do = (si.bf16_bits_to_f64(x) for x in (q, k, v, do))
+        t0 = time.perf_counter()
+        bref.backward_head(q, k, v, do, wl.scale, True)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    flops = cm.attention_bwd_flops(1, heads, wl.Tq, wl.Tk, wl.d, True)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} whole heads (4096x4096 causal, d=128) of {PREFILL}, "
+                      f"{elapsed:.1f} s of fp64 numpy; FLOPs counted as 2.5 x 4*T*T*d/2 per head"}
+
+
+def measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse):
+    """The attention backward on the forward workload: dO from the seeded generator, O and LSE
+    from fa_fwd; warm-up, then timed calls bracketed by HIP events on the launch stream."""
+    do = upload(si.make_grad(wp, seed=0))
+    fa.fa_fwd(pq, pk, pv, causal=True, scale=wp.scale, o=po, lse=plse)
+    dq, dk, dv = torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)
+    ws = torch.empty(fa.fa_bwd_workspace_size(wp.B, wp.h, wp.Tq), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        fa.fa_bwd(pq, pk, pv, po, do, plse, causal=True, scale=wp.scale, dq=dq, dk=dk, dv=dv,
+                  workspace=ws)
+
+    W, K = 3, max(1, args.bwd_steps)
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(t) / K
+    flops = cm.attention_bwd_flops(wp.B, wp.h, wp.Tq, wp.Tk, wp.d, True)
+    tflops = flops / (ms * 1e-3) / 1e12
+    executed = cm.attention_bwd_executed_flops(wp.B, wp.h, wp.Tq, wp.Tk, wp.d, True)
+    peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
+    eprint(f"[bench] backward avg {ms:.4f} ms  {tflops:.1f} TFLOP/s (2.5x fwd FLOPs)  "
+           f"{100 * tflops / peak:.1f}% of {peak:.0f}; executed MFMA rate "
+           f"{executed / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    res = {"metric": "attention backward TFLOP/s (dQ, dK, dV; 2.5x forward FLOPs)",
+           "value": tflops, "unit": "TFLOP/s", "steps": K, "warmup": W,
+           "avg_ms": ms, "min_ms": min(t), "median_ms": sorted(t)[K // 2],
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                        "frac": tflops / peak,
+                        "traffic": traffic_from_profiles(f"fa_bwd__{PREFILL}")},
+           "executed_mfma_tflops": executed / (ms * 1e-3) / 1e12,
+           "config": {"B": wp.B, "h": wp.h, "T": wp.Tq, "d_head": wp.d, "causal": True,
+                      "flops": flops, "executed_flops": executed,
+                      "alg_bytes": cm.attention_bwd_io_bytes(wp.B, wp.h, wp.Tq, wp.Tk, wp.d)}}
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the CPU backward oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_backward(min(args.cpu_seconds, 15.0))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="run one half of the step (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separately timed backward measurement")
+    ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
@@ -128,10 +212,11 @@ def main():
 
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
+    do_backward = args.only == "backward" or (args.only is None and not args.no_backward)
     wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
 
     t0 = time.perf_counter()
-    if do_prefill:
+    if do_prefill or do_backward:
         q, k, v = si.make_inputs(wp, seed=0)
         pq, pk, pv = upload(q), upload(k), upload(v)
         po = torch.empty_like(pq)
@@ -156,6 +241,18 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         eprint(f"[bench] copy probe of {n} bytes done")
+
+    if args.only == "backward":
+        out = {"metric": "attention backward TFLOP/s (2.5x forward FLOPs), % MFMA peak",
+               "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "bf16", "data": "synthetic"}
+        bwd = measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse)
+        out.update(value=bwd["value"], unit=bwd["unit"], roofline=bwd["roofline"],
+                   steps=bwd["steps"], warmup=bwd["warmup"], ms_per_step=bwd["avg_ms"],
+                   config={"workload": PREFILL, "backward": bwd["config"]},
+                   cpu_baseline=bwd.get("cpu_baseline"))
+        print(json.dumps(out), flush=True)
+        return
 
     def step(evs=None, i=0):
         if do_prefill:
@@ -235,6 +332,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    if do_backward:
+        out["backward"] = measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse)
     print(json.dumps(out), flush=True)
 
 

@@ -43,6 +43,27 @@ def attention_io_bytes(B, h, Tq, Tk, d, elem_bytes=2, lse_bytes=4) -> float:
     return (elem_bytes * B * h * d * (2 * Tq + 2 * Tk)) + lse_bytes * B * h * Tq
 
 
+def attention_bwd_flops(B, h, Tq, Tk, d, causal) -> float:
+    """Algorithmic FLOPs of the backward: five contractions per (query, key) pair, 2*d each.
+
+    Page "Chapter 10 Writing and Benchmarking Custom Kernels", §10.3.2: the backward recomputes
+    S = Q K^T and forms dP = dO V^T, dV = P^T dO, dK = dS^T Q and dQ = dS K, so it costs 2.5x the
+    forward's two contractions; causal keeps about half of the pairs.
+    """
+    return 2.5 * attention_flops(B, h, Tq, Tk, d, causal)
+
+
+def attention_bwd_executed_flops(B, h, Tq, Tk, d, causal) -> float:
+    """MFMA FLOPs the two gradient kernels issue: S and dP are formed in both the key-block
+    (dK, dV) and the query-block (dQ) kernel, so seven contractions instead of five."""
+    return 3.5 * attention_flops(B, h, Tq, Tk, d, causal)
+
+
+def attention_bwd_io_bytes(B, h, Tq, Tk, d, elem_bytes=2, lse_bytes=4) -> float:
+    """Backward lower bound: Q, O, dO and K, V read once, LSE read once, dQ, dK, dV written once."""
+    return elem_bytes * B * h * d * (4 * Tq + 4 * Tk) + lse_bytes * B * h * Tq
+
+
 def decode_kv_bytes_per_token(d, elem_bytes=2) -> int:
     """K + V bytes of one cached token of one head: 2 * d * elem."""
     return 2 * d * elem_bytes

@@ -23,7 +23,11 @@
 //     partial sums, so the result is deterministic.
 //   * A tile's 16-byte chunks are XOR-swizzled by row so that both the row reads (16 rows x one
 //     chunk per 16 lanes) and the transposing reads (4 rows x 4 chunks per 32 lanes) hit
-//     distinct LDS banks; tiles are filled by direct global-to-LDS loads, two tiles ahead.
+//     distinct LDS banks; tiles are filled by direct global-to-LDS loads into a ring of stages,
+//     several tiles ahead.
+//   * Each gradient kernel is a software pipeline with one wave per SIMD (see below): the
+//     exp / dS work of one tile is scheduled between the MFMAs of the gradient products of the
+//     tile before, and every MFMA operand streams from LDS through a register ring.
 //   * Ragged tails: buffer loads return zeros past the end of a head, so out-of-range rows
 //     contribute nothing; out-of-range keys and causally hidden entries get P = 0.
 //   * MFMA v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (round to nearest
@@ -40,11 +44,10 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;     // rows of a streamed tile
-constexpr int kStages = 4;    // LDS ring depth
 constexpr int kOwn = 128;     // own rows (keys or queries) per workgroup
 constexpr int kWaves = 4;     // one wave per SIMD, 32 own rows each
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 8;      // MFMA operands in flight
 
 struct BwdParams {
   const uint16_t* q;
@@ -52,7 +55,7 @@ struct BwdParams {
   const uint16_t* v;
   const uint16_t* dout;
   const float* l2;   // LSE_i * log2(e), [BH][Tq]
-  const float* dd;   // D_i = <dO_i, O_i>, [BH][Tq]
+  const float* dd;   // -D_i = -<dO_i, O_i>, [BH][Tq]
   void* dq;
   void* dk;
   void* dv;
@@ -62,13 +65,14 @@ struct BwdParams {
   float scale;
 };
 
-template <int D>
+// A streamed tile of ROWS rows of D bf16 and how the 4 waves load it.
+template <int D, int ROWS>
 struct BTile {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
-  static constexpr int TILE = kRows * D;             // bf16 per tile
+  static constexpr int TILE = ROWS * D;              // bf16 per tile
   static constexpr uint32_t BYTES = TILE * 2;
   static constexpr int ROWS_PER_LOAD = 64 / CH;      // rows one 64-lane 1 KB load covers
-  static constexpr int LOADS = kRows / ROWS_PER_LOAD;
+  static constexpr int LOADS = ROWS / ROWS_PER_LOAD;
   static constexpr int LPW = LOADS / kWaves;         // 1 KB loads per wave per tile
   static_assert(LPW >= 1 && LOADS % kWaves == 0, "staging layout");
   // Row term of the chunk swizzle (physical chunk = logical chunk ^ f(r), an involution).
@@ -80,20 +84,20 @@ struct BTile {
   }
 };
 
-template <int D>
+// Per-lane byte offsets inside a tile (add the tile's LDS address; tiles are 1 KB-aligned).
+//  Row operand (MFMA A operand from a row-major tile): tile row 32*blk + r32, logical chunk
+//  2*s + g; the swizzle makes this row_off ^ (32*s), plus blk * 32 rows.
+//  Transposed operand (A operand = tile^T, 32-column block db, k-step ks, half hf): lane l of
+//  16-lane group (g, dh) addresses row 16*ks + 8*hf + 4*g + (l % 16) / 4, column
+//  32*db + 16*dh + 4*(l % 4), and receives tile^T row 32*db + (l % 32) at rows
+//  16*ks + 8*hf + 4*g + 0..3.  The swizzle depends on the row through (l % 16) / 4, g and hf
+//  only, which makes this (tr_off ^ (64*db) ^ (32*hf)) + (16*ks + 8*hf) rows.
+template <int D, int ROWS>
 struct Lanes {
-  // Per-lane byte offsets inside a tile (add the tile's LDS address; stages are 1 KB-aligned).
-  //  Row operand (MFMA A operand from a row-major tile): tile row 32*blk + r32, logical chunk
-  //  2*s + g; the swizzle makes this row_off ^ (32*s), plus blk * 32 rows.
-  //  Transposed operand (A operand = tile^T, 32-column block db, k-step ks, half hf): lane l of
-  //  16-lane group (g, dh) addresses row 16*ks + 8*hf + 4*g + (l % 16) / 4, column
-  //  32*db + 16*dh + 4*(l % 4), and receives tile^T row 32*db + (l % 32) at rows
-  //  16*ks + 8*hf + 4*g + 0..3.  The swizzle depends on the row through (l % 16) / 4, g and hf
-  //  only, which makes this (tr_off ^ (64*db) ^ (32*hf)) + (16*ks + 8*hf) rows.
+  using T = BTile<D, ROWS>;
   uint32_t row_off, tr_off;
-  uint32_t dma_l[BTile<D>::LPW], dma_g[BTile<D>::LPW];   // LDS / global offsets of loads
+  uint32_t dma_l[T::LPW], dma_g[T::LPW];   // LDS / global byte offsets of this wave's loads
   __device__ __forceinline__ Lanes(int wave, int lane) {
-    using T = BTile<D>;
     const int g = lane >> 5, r32 = lane & 31;
     row_off = 2u * (uint32_t)(r32 * D) + 16u * (uint32_t)(g ^ T::f(r32));
     const int x = (lane & 15) >> 2, dh = (lane >> 4) & 1, b = (lane & 3) >> 1;
@@ -111,16 +115,36 @@ struct Lanes {
   }
 };
 
+// Per-lane LDS addresses of one region (a ring of tiles at `base`): the row operand of k-step s
+// and the transposed operand halves of column block db are base + row[s] and base + tr[db][hf];
+// the stage, the 32-row block and the k-step add byte offsets that are compile-time constants,
+// which the LDS instructions take as immediates.
 template <int D>
-__device__ __forceinline__ bf16x8_t row_opnd(uint32_t at, int blk, int s) {
-  return lds_read_bf16x8((at ^ (32u * (uint32_t)s)) + (uint32_t)blk * (32u * D * 2u));
-}
-template <int D>
-__device__ __forceinline__ bf16x8_t tr_opnd(uint32_t at, int db, int ks) {
-  const uint32_t a = at ^ (64u * (uint32_t)db);
-  return lds_read_tr_pair(a + (uint32_t)(16 * ks) * (D * 2u),
-                          (a ^ 32u) + (uint32_t)(16 * ks + 8) * (D * 2u));
-}
+struct Region {
+  static constexpr uint32_t kRowBlock = 32u * D * 2u;   // bytes of 32 tile rows
+  uint32_t row[D / 16], tr[D / 32][2];
+  __device__ __forceinline__ Region(uint32_t base, uint32_t row_off, uint32_t tr_off) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) row[s] = base + (row_off ^ (32u * (uint32_t)s));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        tr[db][hf] = base + (tr_off ^ (64u * (uint32_t)db) ^ (32u * (uint32_t)hf));
+  }
+  // A operand: rows 32*blk + (lane % 32), k-step s, of the tile at byte offset so
+  __device__ __forceinline__ bf16x8_t row_opnd(uint32_t so, int blk, int s) const {
+    return lds_read_bf16x8(row[s] + so + (uint32_t)blk * kRowBlock);
+  }
+  // A operand = tile^T: rows 32*db + (lane % 32), k-step ks (16 tile rows)
+  __device__ __forceinline__ bf16x8_t tr_opnd(uint32_t so, int db, int ks) const {
+    return lds_read_tr_pair(tr[db][0] + so + (uint32_t)(16 * ks) * (D * 2u),
+                            tr[db][1] + so + (uint32_t)(16 * ks + 8) * (D * 2u));
+  }
+};
+
+template <int ST>
+using Stage = std::integral_constant<int, ST>;
 
 // Stores 4 consecutive columns of one row (fp32 or rounded to bf16).
 template <bool OUT_F32>
@@ -135,9 +159,8 @@ __device__ __forceinline__ void store4(void* base, size_t elem, float a, float b
 
 // Workgroup n -> (head, own block).  With groups == 8 the workgroups dispatched to one XCD
 // (n % 8) take the blocks of heads n % 8, n % 8 + 8, ... in order, so the tiles a head streams
-// are shared in that XCD's L2; `heavy_first_desc` reverses the block order within a head.
-__device__ __forceinline__ void block_of(const BwdParams& p, bool heavy_last_blocks, int& bh,
-                                         int& blk) {
+// are shared in that XCD's L2; `reverse` runs a head's blocks from the last one.
+__device__ __forceinline__ void block_of(const BwdParams& p, bool reverse, int& bh, int& blk) {
   const int n = blockIdx.x;
   int hl, j;
   if (p.groups == 8) {
@@ -150,11 +173,11 @@ __device__ __forceinline__ void block_of(const BwdParams& p, bool heavy_last_blo
     j = n - hl * p.nblk;
   }
   bh = __builtin_amdgcn_readfirstlane(hl);
-  blk = __builtin_amdgcn_readfirstlane(heavy_last_blocks ? p.nblk - 1 - j : j);
+  blk = __builtin_amdgcn_readfirstlane(reverse ? p.nblk - 1 - j : j);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Preprocess: D_i = <dO_i, O_i> (fp32 sum of bf16 products) and LSE_i * log2(e).
+// Preprocess: -D_i = -<dO_i, O_i> (fp32 sum of bf16 products) and LSE_i * log2(e).
 // One row per D/8 lanes (16 bytes each); rows = B * h * Tq.
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __restrict__ o,
@@ -177,7 +200,7 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (row < rows && part == 0) {
-    dd[row] = acc;
+    dd[row] = -acc;
     l2[row] = lse[row] * kLog2e;
   }
 }
@@ -188,26 +211,35 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 //   V: the elementwise part, P = exp2(S * scale * log2 e - L2), dS = P (dP - D), rounded to bf16;
 //   C: the gradient products that consume P and dS, from transposed operands in LDS.
 // Step s runs C of tile s - 1 with V of tile s scheduled between its MFMAs (one wave per SIMD:
-// the vector instructions issue while the matrix core works), then A of tile s + 1.  V of tile s
-// reads the score registers A filled in the previous step and writes the bf16 operands of the
-// next step's C, which are handed over by register moves at the end of the step.  Every MFMA
-// operand streams from LDS through a ring of kRing registers, each read issued kRing MFMAs ahead
-// of its use.  Tiles go through a 4-stage LDS ring: at step s, tile s + 2 is requested into the
-// stage tile s - 2 left (its last use, C of step s - 1, is behind the barrier that ended that
-// step), and the step ends once it has landed.
-constexpr int kRing = 8;
+// the vector instructions issue while the matrix core works), then A of tile s + 1; V of tile s
+// reads the score registers that A filled in the step before.  The bf16 P / dS operands are
+// double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring of kRing
+// registers, each read issued kRing MFMAs ahead of its use, and the ring runs across steps: the
+// last MFMAs of step s read the first operands of step s + 1 (C operands of tile s, resident),
+// before the barrier that ends the step.  Tiles are loaded AHEAD steps ahead into a ring of NST
+// stages; the stage of every step is a compile-time constant (the steady-state loop dispatches
+// on s % NST), so that all LDS addresses are per-lane registers plus immediates.  The last two
+// steps run all three parts: their V and A parts read stages holding stale tiles and produce
+// values that are never used.
 
 // A step's MFMA stream: NC C-part MFMAs (two transposing reads each), then NA A-part MFMAs (one
-// LDS read each); VPM vector instructions are scheduled after each C-part MFMA (after each
-// A-part MFMA when there is no C part), and the step issues XR extra LDS reads up front.
-template <int NC, int NA, int VPM, int XR>
+// read each).  PRE: the ring arrived preloaded; NEXT: the last kRing MFMAs read the next step's
+// first operands (C operands, two reads each).  VPM vector instructions are scheduled after each
+// C-part MFMA (after each A-part MFMA when the step has no C part), and XR extra LDS reads are
+// issued up front.
+template <int NC, int NA, int VPM, int XR, bool PRE, bool NEXT>
 struct StepSeq {
   static constexpr int n = NC + NA;
+  static_assert(n % kRing == 0, "the ring restarts at slot 0 every step");
   static constexpr __device__ int reads(int i) { return i < NC ? 2 : 1; }
+  static constexpr __device__ int refill_reads(int i) {
+    return i + kRing < n ? reads(i + kRing) : (NEXT ? 2 : 0);
+  }
   static constexpr __device__ int valu(int i) { return (NC > 0 ? i < NC : i < NA) ? VPM : 0; }
   static constexpr __device__ int initial_reads() {
     int r = XR;
-    for (int i = 0; i < kRing && i < n; ++i) r += reads(i);
+    if (!PRE)
+      for (int i = 0; i < kRing && i < n; ++i) r += reads(i);
     return r;
   }
 };
@@ -216,8 +248,8 @@ template <class S, int I>
 __device__ __forceinline__ void sched_step() {
   if constexpr (I < S::n) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA I
-    if constexpr (I + kRing < S::n)
-      __builtin_amdgcn_sched_group_barrier(0x100, S::reads(I + kRing), 0);   // its ring refill
+    if constexpr (S::refill_reads(I) > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, S::refill_reads(I), 0);   // its ring refill
     if constexpr (S::valu(I) > 0) __builtin_amdgcn_sched_group_barrier(0x002, S::valu(I), 0);
     sched_step<S, I + 1>();
   }
@@ -229,8 +261,8 @@ __device__ __forceinline__ void sched_pattern() {
   sched_step<S, 0>();
 }
 
-// Packs registers 8*(ks%2) .. +7 of a 16-register MFMA result block into one bf16 B operand
-// (RNE): the 16 streamed rows of k-step ks.
+// Packs registers 8*half .. +7 of a 16-register MFMA result block into one bf16 B operand
+// (RNE): the 16 streamed rows of one k-step.
 __device__ __forceinline__ bf16x8_t pack_kstep(const f32x16_t& x, int half) {
   const int b0 = 8 * half;
   const u32x2_t lo = pack_bf16x4(x[b0], x[b0 + 1], x[b0 + 2], x[b0 + 3]);
@@ -238,39 +270,59 @@ __device__ __forceinline__ bf16x8_t pack_kstep(const f32x16_t& x, int half) {
   return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// Parts of a step: C (gradient products of tile s - 1), V (elementwise part of tile s),
+// A (score products of tile s + 1), M (V applies the mask).
 template <bool C, bool V, bool A, bool M>
 struct Parts {
   static constexpr bool c = C, v = V, a = A, m = M;
 };
 
+// Waits until this wave's loads of tile `need` have landed, when tiles up to `last` have been
+// requested (each tile is `per` vector-memory operations; they complete in issue order).
+template <int PER, int AHEAD>
+__device__ __forceinline__ void wait_tile(int need, int last) {
+  const int after = min(AHEAD, max(0, last - need));
+  static_assert(AHEAD <= 2, "wait_tile handles up to two later tiles");
+  if (after >= 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+  else if (after == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (128-key block, head), lane = key.
+// dK, dV: one workgroup per (128-key block, head), lane = key; query tiles of 32 rows.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-  using T = BTile<D>;
+  constexpr int R = 32;        // query rows per streamed tile (one 32-row MFMA block)
+  constexpr int NST = 8;       // LDS stages
+  constexpr int AHEAD = 4;     // step s requests tile s + AHEAD
+  using T = BTile<D, R>;
   constexpr int NS = D / 16;   // k-steps over d
   constexpr int ND = D / 32;   // 32-row blocks of dK^T / dV^T
-  constexpr int NA = 4 * NS;   // S and dP MFMAs per tile
-  constexpr int NC = 8 * ND;   // dV^T and dK^T MFMAs per tile
-  // LDS: Q stages, dO stages, then 64 floats of L2 and of D per stage.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
-  __shared__ __attribute__((aligned(256))) float lds_ld[2 * kStages * kRows];
+  constexpr int NA = 2 * NS;   // S and dP MFMAs per tile
+  constexpr int NC = 4 * ND;   // dV^T and dK^T MFMAs per tile (two 16-query k-steps)
+  constexpr int LDS_LD = 64;   // floats of L2 (and of -D) per stage (one 64-lane load)
+  // LDS: Q stages, dO stages, then L2 and -D per stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
+  __shared__ __attribute__((aligned(256))) float lds_ld[2 * NST * LDS_LD];
   const uint32_t lq = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  const uint32_t ldo = lq + kStages * T::BYTES;
+  const uint32_t ldo = lq + NST * T::BYTES;
   const uint32_t ll = (uint32_t)reinterpret_cast<uintptr_t>(lds_ld);
-  const uint32_t ld = ll + kStages * kRows * 4;
+  const uint32_t ld = ll + NST * LDS_LD * 4;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, r32 = lane & 31;
-  const Lanes<D> ln(wave, lane);
+  const int g = lane >> 5;
+  const Lanes<D, R> ln(wave, lane);
 
   int bh, blk;
   block_of(p, false, bh, blk);
   const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
   const int kw0 = blk * kOwn + wave * 32;   // this wave's first key
-  const int key = kw0 + r32;
+  const int key = kw0 + (lane & 31);
   // P is zeroed for queries below thr: keys past the end see nothing; causal keys see queries
   // from key - off on
   const int thr = key >= p.Tk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
@@ -291,8 +343,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 
   // query tiles this block needs: from the first query that sees its first key
-  const int nqt = (p.Tq + kRows - 1) / kRows;
-  const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwn - off) / kRows) : 0;
+  const int nqt = (p.Tq + R - 1) / R;
+  const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwn - off) / R) : 0;
   const int nt = nqt - t0;
 
   const u32x4_t rq = rsrc_words(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
@@ -300,19 +352,21 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       rsrc_words(p.dout + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
   const u32x4_t rl = rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
   const u32x4_t rd = rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
-  auto request = [&](int it) {   // tile t0 + it into stage it % kStages
-    const int st = it & (kStages - 1);
-    const uint32_t g0 = (uint32_t)(t0 + it) * (kRows * D * 2);
+  auto request = [&](int it) {   // tile t0 + it into stage it % NST
+    const int st = it & (NST - 1);
+    const uint32_t g0 = (uint32_t)(t0 + it) * (R * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
       lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
       lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
     }
-    // every wave writes the same 64 values of L2 and D (identical data, so the copies agree)
-    const uint32_t r0 = (uint32_t)((t0 + it) * kRows + lane) * 4u;
-    lds_dma4(rl, ll + st * (kRows * 4), r0);
-    lds_dma4(rd, ld + st * (kRows * 4), r0);
+    // every wave writes the same 64 values of L2 and -D from the tile's first row on
+    // (identical data, so the copies agree; the tile uses the first 32)
+    const uint32_t r0 = (uint32_t)((t0 + it) * R + lane) * 4u;
+    lds_dma4(rl, ll + st * (LDS_LD * 4), r0);
+    lds_dma4(rd, ld + st * (LDS_LD * 4), r0);
   };
+  constexpr int PER = 2 * T::LPW + 2;   // vector-memory operations per tile and wave
 
   f32x16_t accv[ND], acck[ND];
 #pragma unroll
@@ -320,105 +374,118 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     accv[db] = f32x16_t{};
     acck[db] = f32x16_t{};
   }
-  f32x16_t sacc[2], dpacc[2];   // [32-query block]: S then P, dP then dS
-  bf16x8_t pb[4], dsb[4];       // P and dS of the previous tile (C operands)
+  f32x16_t sacc, dpacc;           // S then P, dP - D then dS (32 queries x this key)
+  bf16x8_t pb[2][2], dsb[2][2];   // [tile parity][k-step]: P and dS as C operands
   bf16x8_t ring[kRing];
+  const Region<D> rQ(lq, ln.row_off, ln.tr_off), rO(ldo, ln.row_off, ln.tr_off);
 
-  // Step s (see the pipeline above).  In the MFMA result layout, register i of 32-query block
-  // qb holds query 64*(t0 + s) + 32*qb + 8*(i/4) + 4*g + i%4 for key `key`.
-  auto step = [&](auto parts, const int s) {
+  // Step s with stage ST = s % NST.  In the MFMA result layout, register i holds query
+  // R*(t0 + s) + 8*(i/4) + 4*g + i%4 for key `key`.
+  auto step = [&](auto parts, auto stage, const int s) {
     using PT = decltype(parts);
+    constexpr int ST = decltype(stage)::value;
     constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-    using S = StepSeq<nc, na, PT::v ? 7 : 0, PT::v ? 16 : 0>;
-    if (s + 2 < nt) request(s + 2);
-    const uint32_t qc = lq + ((s - 1) & 3) * T::BYTES + ln.tr_off;
-    const uint32_t doc = ldo + ((s - 1) & 3) * T::BYTES + ln.tr_off;
-    const uint32_t qa = lq + ((s + 1) & 3) * T::BYTES + ln.row_off;
-    const uint32_t doa = ldo + ((s + 1) & 3) * T::BYTES + ln.row_off;
-    auto opnd = [&](int i) -> bf16x8_t {
-      if (i < nc) {
-        const int r = i % (2 * ND);
-        return tr_opnd<D>((r & 1) ? qc : doc, r >> 1, i / (2 * ND));
-      }
-      const int j = i - nc;
-      return row_opnd<D>((j & 1) ? doa : qa, (j >> 1) & 1, j >> 2);
+    constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+    using S = StepSeq<nc, na, PT::v ? 6 : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next>;
+    constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+    constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
+    constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
+    constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // operand parities
+    if (s + AHEAD < nt) request(s + AHEAD);
+    // C operand i of the tile at byte offset so: k-step i / (2 ND), column block, Q or dO
+    auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t {
+      const int r = i % (2 * ND);
+      return ((r & 1) ? rQ : rO).tr_opnd(so, r >> 1, i / (2 * ND));
     };
+    auto opnd = [&](int i) -> bf16x8_t {
+      if (i < nc) return c_opnd(so_c, i);
+      const int j = i - nc;
+      return ((j & 1) ? rO : rQ).row_opnd(so_a, 0, j >> 1);
+    };
+    if constexpr (!PT::c) {
 #pragma unroll
-    for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
-    bf16x8_t pn[4], dsn[4];
+      for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+    }
     if constexpr (PT::v) {
-      const uint32_t lo = ll + (s & 3) * (kRows * 4), dof = ld + (s & 3) * (kRows * 4);
-      f32x4_t L4[2][4], D4[2][4];
+      // dpacc holds dP - D (its A part started from -D)
+      f32x4_t L4[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int a = 0; a < 4; ++a)
+        L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
+      const int q0 = (t0 + s) * R + 4 * g;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t o4 = 4u * (uint32_t)(32 * qb + 8 * a + 4 * g);
-          L4[qb][a] = lds_read_f32x4(lo + o4);
-          D4[qb][a] = lds_read_f32x4(dof + o4);
-        }
-      const int q0 = (t0 + s) * kRows + 4 * g;
+      for (int i = 0; i < 16; ++i) {
+        const int a = i >> 2, e = i & 3;
+        float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
+        if (q0 + 8 * a + e < thr) pv = 0.f;
+        sacc[i] = pv;
+        dpacc[i] = pv * dpacc[i];
+      }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int ks = 0; ks < 2; ++ks) {
+        pb[PV][ks] = pack_kstep(sacc, ks);
+        dsb[PV][ks] = pack_kstep(dpacc, ks);
+      }
+    }
+    // the next tile's dP accumulator starts from -D of its rows
+    f32x16_t nd0;
+    if constexpr (PT::a) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int a = i >> 2, e = i & 3;
-          float pv = fast_exp2(__builtin_fmaf(sacc[qb][i], p.c, -L4[qb][a][e]));
-          if (q0 + 32 * qb + 8 * a + e < thr) pv = 0.f;
-          sacc[qb][i] = pv;
-          dpacc[qb][i] = pv * (dpacc[qb][i] - D4[qb][a][e]);
-        }
+      for (int a = 0; a < 4; ++a) {
+        const f32x4_t v4 = lds_read_f32x4(ld + ((ST + 1) % NST) * (LDS_LD * 4) +
+                                          4u * (uint32_t)(8 * a + 4 * g));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        pn[ks] = pack_kstep(sacc[ks >> 1], ks & 1);
-        dsn[ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+        for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
       }
     }
 #pragma unroll
     for (int i = 0; i < S::n; ++i) {
       const bf16x8_t a = ring[i % kRing];
-      if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+      if (i + kRing < S::n)
+        ring[i % kRing] = opnd(i + kRing);
+      else if (next)
+        ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
       if (i < nc) {
         const int r = i % (2 * ND), ks = i / (2 * ND);
         if (r & 1)
-          acck[r >> 1] = mfma_32x32x16(a, dsb[ks], acck[r >> 1]);
+          acck[r >> 1] = mfma_32x32x16(a, dsb[PC][ks], acck[r >> 1]);
         else
-          accv[r >> 1] = mfma_32x32x16(a, pb[ks], accv[r >> 1]);
+          accv[r >> 1] = mfma_32x32x16(a, pb[PC][ks], accv[r >> 1]);
       } else {
-        const int j = i - nc, ss = j >> 2, qb = (j >> 1) & 1;
-        const bool first = ss == 0;
+        const int j = i - nc, ss = j >> 1;
         if (j & 1)
-          dpacc[qb] = mfma_32x32x16(a, vf[ss], first ? f32x16_t{} : dpacc[qb]);
+          dpacc = mfma_32x32x16(a, vf[ss], ss == 0 ? nd0 : dpacc);
         else
-          sacc[qb] = mfma_32x32x16(a, kf[ss], first ? f32x16_t{} : sacc[qb]);
+          sacc = mfma_32x32x16(a, kf[ss], ss == 0 ? f32x16_t{} : sacc);
       }
     }
     sched_pattern<S>();
-    if constexpr (PT::v) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        pb[ks] = pn[ks];
-        dsb[ks] = dsn[ks];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile s + 2 has landed (this wave's part)
+    // the next step's A part reads tile s + 2
+    wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
     __syncthreads();
   };
 
-  request(0);
-  if (nt > 1) request(1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
+  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and K, V rows)
   __syncthreads();
-  // steps -1 .. nt: A of tile 0; then C of s - 1, V of s, A of s + 1; then the last C
-  step(Parts<false, false, true, false>{}, -1);
-  if (nt > 1) {
-    step(Parts<false, true, true, false>{}, 0);
-    for (int s = 1; s + 1 < nt; ++s) step(Parts<true, true, true, false>{}, s);
-    step(Parts<true, true, false, false>{}, nt - 1);
-  } else {
-    step(Parts<false, true, false, false>{}, 0);
+  // steps -1 .. nt (see the pipeline above)
+  step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
+  step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+  // steps 1 .. nt: a chain of the NST stage variants, left after step nt
+  {
+    using P = Parts<true, true, true, true>;
+    int s = 1;
+    for (;;) {
+      step(P{}, Stage<1>{}, s); if (++s > nt) break;
+      step(P{}, Stage<2>{}, s); if (++s > nt) break;
+      step(P{}, Stage<3>{}, s); if (++s > nt) break;
+      step(P{}, Stage<4>{}, s); if (++s > nt) break;
+      step(P{}, Stage<5>{}, s); if (++s > nt) break;
+      step(P{}, Stage<6>{}, s); if (++s > nt) break;
+      step(P{}, Stage<7>{}, s); if (++s > nt) break;
+      step(P{}, Stage<0>{}, s); if (++s > nt) break;
+    }
   }
-  step(Parts<true, false, false, false>{}, nt);
 
   // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
   if (key < p.Tk) {
@@ -437,36 +504,39 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup per (128-query block, head), lane = query.
+// dQ: one workgroup per (128-query block, head), lane = query; key tiles of 64 rows.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  using T = BTile<D>;
+  constexpr int R = 64;        // keys per streamed tile (two 32-row MFMA blocks)
+  constexpr int NST = 4;       // LDS stages
+  constexpr int AHEAD = 2;     // step s requests tile s + AHEAD
+  using T = BTile<D, R>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int NA = 4 * NS;   // S^T and dP^T MFMAs per tile
-  constexpr int NC = 4 * ND;   // dQ^T MFMAs per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * T::TILE];
+  constexpr int NC = 4 * ND;   // dQ^T MFMAs per tile (four 16-key k-steps)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  const uint32_t lv = lk + kStages * T::BYTES;
+  const uint32_t lv = lk + NST * T::BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, r32 = lane & 31;
-  const Lanes<D> ln(wave, lane);
+  const int g = lane >> 5;
+  const Lanes<D, R> ln(wave, lane);
 
   int bh, blk;
   block_of(p, CAUSAL, bh, blk);   // causal: the longest key ranges (last query blocks) first
   const int off = p.Tk - p.Tq;
   const int i0 = blk * kOwn;
   const int qw0 = i0 + wave * 32;
-  const int qrow = qw0 + r32;
+  const int qrow = qw0 + (lane & 31);
   // keys above lim get P = 0 (past the end, or above the diagonal)
   const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
 
-  // Q and dO rows of this lane's query as B operands, and its L2 and D.
+  // Q and dO rows of this lane's query as B operands, and its L2 and -D.
   bf16x8_t qf[NS], dof[NS];
-  float l2q = 0.f, dq_d = 0.f;
+  float l2q = 0.f, ndq = 0.f;
   {
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
@@ -480,108 +550,109 @@ void fa_bwd_dq_kernel(BwdParams p) {
     }
     if (qrow < p.Tq) {
       l2q = p.l2[(size_t)bh * p.Tq + qrow];
-      dq_d = p.dd[(size_t)bh * p.Tq + qrow];
+      ndq = p.dd[(size_t)bh * p.Tq + qrow];
     }
   }
 
   int kend = p.Tk;
   if (CAUSAL) kend = min(p.Tk, min(i0 + kOwn, p.Tq) + off);
-  const int nt = __builtin_amdgcn_readfirstlane((kend + kRows - 1) / kRows);
+  const int nt = __builtin_amdgcn_readfirstlane((kend + R - 1) / R);
 
   const u32x4_t rk = rsrc_words(p.k + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
   const u32x4_t rv = rsrc_words(p.v + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
   auto request = [&](int it) {
-    const int st = it & (kStages - 1);
-    const uint32_t g0 = (uint32_t)it * (kRows * D * 2);
+    const int st = it & (NST - 1);
+    const uint32_t g0 = (uint32_t)it * (R * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
       lds_dma16(rk, lk + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
       lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
     }
   };
+  constexpr int PER = 2 * T::LPW;
 
   f32x16_t accq[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) accq[db] = f32x16_t{};
   f32x16_t sacc[2], dpacc[2];   // [32-key block]: S^T, dP^T (then dS^T)
-  bf16x8_t dsb[4], ring[kRing];
+  bf16x8_t dsb[2][4];           // [tile parity][k-step]: dS^T as C operands
+  bf16x8_t ring[kRing];
+  const Region<D> rK(lk, ln.row_off, ln.tr_off), rV(lv, ln.row_off, ln.tr_off);
 
-  // Step s.  Register i of 32-key block kb holds key 64*s + 32*kb + 8*(i/4) + 4*g + i%4 for
-  // query `qrow`.
-  auto step = [&](auto parts, const int s) {
+  // Step s with stage ST = s % NST.  Register i of 32-key block kb holds key
+  // 64*s + 32*kb + 8*(i/4) + 4*g + i%4 for query `qrow`.
+  auto step = [&](auto parts, auto stage, const int s) {
     using PT = decltype(parts);
+    constexpr int ST = decltype(stage)::value;
     constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-    using S = StepSeq<nc, na, PT::v ? (PT::m ? 12 : 8) : 0, 0>;
-    if (s + 2 < nt) request(s + 2);
-    const uint32_t kc = lk + ((s - 1) & 3) * T::BYTES + ln.tr_off;
-    const uint32_t ka = lk + ((s + 1) & 3) * T::BYTES + ln.row_off;
-    const uint32_t va = lv + ((s + 1) & 3) * T::BYTES + ln.row_off;
+    constexpr bool next = PT::v;
+    using S = StepSeq<nc, na, PT::v ? (PT::m ? 13 : 9) : 0, 0, PT::c, next>;
+    constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;
+    constexpr uint32_t so_v = ST * T::BYTES;
+    constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;
+    constexpr int PC = (ST + 1) & 1, PV = ST & 1;
+    if (s + AHEAD < nt) request(s + AHEAD);
+    auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rK.tr_opnd(so, i % ND, i / ND); };
     auto opnd = [&](int i) -> bf16x8_t {
-      if (i < nc) return tr_opnd<D>(kc, i % ND, i / ND);
+      if (i < nc) return c_opnd(so_c, i);
       const int j = i - nc;
-      return row_opnd<D>((j & 1) ? va : ka, (j >> 1) & 1, j >> 2);
+      return ((j & 1) ? rV : rK).row_opnd(so_a, (j >> 1) & 1, j >> 2);
     };
+    if constexpr (!PT::c) {
 #pragma unroll
-    for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
-    bf16x8_t dsn[4];
+      for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+    }
     if constexpr (PT::v) {
-      const int kj0 = s * kRows + 4 * g;
+      const int kj0 = s * R + 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
           if (PT::m && kj0 + 32 * kb + 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
-          dpacc[kb][i] = pv * (dpacc[kb][i] - dq_d);
+          dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
         }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dsn[ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+      for (int ks = 0; ks < 4; ++ks) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
     }
 #pragma unroll
     for (int i = 0; i < S::n; ++i) {
       const bf16x8_t a = ring[i % kRing];
-      if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+      if (i + kRing < S::n)
+        ring[i % kRing] = opnd(i + kRing);
+      else if (next)
+        ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
       if (i < nc) {
-        accq[i % ND] = mfma_32x32x16(a, dsb[i / ND], accq[i % ND]);
+        accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
       } else {
         const int j = i - nc, ss = j >> 2, kb = (j >> 1) & 1;
-        const bool first = ss == 0;
         if (j & 1)
-          dpacc[kb] = mfma_32x32x16(a, dof[ss], first ? f32x16_t{} : dpacc[kb]);
+          dpacc[kb] = mfma_32x32x16(a, dof[ss], ss == 0 ? f32x16_t{} : dpacc[kb]);
         else
-          sacc[kb] = mfma_32x32x16(a, qf[ss], first ? f32x16_t{} : sacc[kb]);
+          sacc[kb] = mfma_32x32x16(a, qf[ss], ss == 0 ? f32x16_t{} : sacc[kb]);
       }
     }
     sched_pattern<S>();
-    if constexpr (PT::v) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dsb[ks] = dsn[ks];
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
     __syncthreads();
   };
-  // tile s needs masking for this wave if a key is past the end or above a query's diagonal
-  auto need_mask = [&](int s) {
-    return (s * kRows + kRows > p.Tk) || (CAUSAL && s * kRows + kRows - 1 > qw0 + off);
-  };
-
-  request(0);
-  if (nt > 1) request(1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
+  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));
   __syncthreads();
-  step(Parts<false, false, true, false>{}, -1);
-  if (nt > 1) {
-    if (need_mask(0)) step(Parts<false, true, true, true>{}, 0);
-    else step(Parts<false, true, true, false>{}, 0);
-    for (int s = 1; s + 1 < nt; ++s) {
-      if (need_mask(s)) step(Parts<true, true, true, true>{}, s);
-      else step(Parts<true, true, true, false>{}, s);
+  step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
+  step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+  // steps 1 .. nt: a chain of the NST stage variants, left after step nt (every step applies
+  // the mask: two more vector instructions per score, and one code path per stage)
+  {
+    using P = Parts<true, true, true, true>;
+    int s = 1;
+    for (;;) {
+      step(P{}, Stage<1>{}, s); if (++s > nt) break;
+      step(P{}, Stage<2>{}, s); if (++s > nt) break;
+      step(P{}, Stage<3>{}, s); if (++s > nt) break;
+      step(P{}, Stage<0>{}, s); if (++s > nt) break;
     }
-    step(Parts<true, true, false, true>{}, nt - 1);
-  } else {
-    step(Parts<false, true, false, true>{}, 0);
   }
-  step(Parts<true, false, false, false>{}, nt);
 
   if (qrow < p.Tq) {
     const size_t row = ((size_t)bh * (size_t)p.Tq + (size_t)qrow) * D;

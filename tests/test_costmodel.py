@@ -109,3 +109,13 @@ def test_north_star_flop_and_byte_formulas():
     assert cm.bf16_peak_at_clock(2.4e9) == pytest.approx(2.5166e15, rel=1e-4)
     assert cm.MI355X_PEAK_BF16_DENSE_FLOPS / cm.MI355X_PEAK_HBM_BYTES_PER_S == pytest.approx(312.5)
     assert math.isclose(cm.decode_workspace_bytes(64, 32, 128, 16), 64 * 32 * 16 * 130 * 4)
+
+
+def test_backward_flops_and_bytes():
+    f = cm.attention_flops(8, 32, 4096, 4096, 128, True)
+    assert cm.attention_bwd_flops(8, 32, 4096, 4096, 128, True) == 2.5 * f
+    assert cm.attention_bwd_executed_flops(8, 32, 4096, 4096, 128, True) == 3.5 * f
+    # five contractions of 2*d FLOPs per pair, all pairs when not causal
+    assert cm.attention_bwd_flops(1, 1, 3, 5, 8, False) == 5 * 2 * 8 * 3 * 5
+    # Q, O, dO, dQ (Tq rows) and K, V, dK, dV (Tk rows) of d bf16, plus the fp32 LSE
+    assert cm.attention_bwd_io_bytes(1, 1, 3, 5, 8) == 2 * 8 * (4 * 3 + 4 * 5) + 4 * 3
