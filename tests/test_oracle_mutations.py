@@ -69,3 +69,29 @@ def test_backward_mutant_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
+
+
+SOFTMAX_SRC = os.path.join(ROOT, "oracle", "softmax_ref.py")
+SOFTMAX_MUTANTS = {
+    "no max subtraction": ("e = np.exp(x - m[:, None])", "e = np.exp(x)"),
+    "sum over the wrong axis": ("s = np.sum(e, axis=1)", "s = np.sum(e, axis=0)[: e.shape[0]]"),
+    "lse without the log": ("return e / s[:, None], m + np.log(s)", "return e / s[:, None], m + s"),
+    "recurrence without the rescale": ("l = l * np.exp(m - m_new) + float(np.sum(np.exp(t - m_new)))",
+                                       "l = l + float(np.sum(np.exp(t - m_new)))"),
+    "recurrence rescale inverted": ("l = l * np.exp(m - m_new) + float(np.sum(np.exp(t - m_new)))",
+                                    "l = l * np.exp(m_new - m) + float(np.sum(np.exp(t - m_new)))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SOFTMAX_MUTANTS))
+def test_softmax_mutant_is_caught(name, tmp_path):
+    old, new = SOFTMAX_MUTANTS[name]
+    src = open(SOFTMAX_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    path = tmp_path / "mutant_softmax.py"
+    path.write_text(src.replace(old, new))
+    env = dict(os.environ, FA_ORACLE_SOFTMAX_MUTANT_FILE=str(path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_softmax.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
