@@ -152,8 +152,29 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
                int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head, int causal,
                float scale, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode and fa_bwd / fa_bwd_f32
- * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return. */
+/*
+ * fa_softmax_rows -- row-wise softmax of a [rows][cols] fp32 matrix, in one pass over HBM.
+ *   x [rows][cols] fp32 (in); y [rows][cols] fp32 (out); lse [rows] fp32 (out, natural log) or
+ *   NULL.  y_ij = exp(x_ij - m_i) / sum_k exp(x_ik - m_i) with m_i the row max, and
+ *   lse_i = m_i + log(sum_k exp(x_ik - m_i)).  The workload of page "Chapter 10 Writing and
+ *   Benchmarking Custom Kernels", section 10.2.2 (the worked example: one block per row, the max
+ *   subtracted before exponentiating), computed with the running (max, sum) recurrence of that
+ *   section's closing question and of page "Kernels -- fusion and FlashAttention", section 3:
+ *   partial sums are rescaled by exp(m_part - m_new) when merged.  Rows of up to 8192 columns
+ *   are read once and written once; wider rows are read twice (the (max, sum) pass, then the
+ *   output pass).
+ *   Entries equal to -inf are masked (y = 0).  A row with no finite entry, or one holding +inf or
+ *   NaN, has no defined softmax and its outputs are unspecified.
+ *   Preconditions: rows, cols >= 1, cols <= INT32_MAX, (rows + 3) / 4 <= INT32_MAX; x, y (and lse)
+ *   4-byte aligned; y must not overlap x.  16-byte aligned x and y with cols % 4 == 0 take the
+ *   vector path.
+ */
+int fa_softmax_rows(const float* x, float* y, float* lse, int64_t rows, int64_t cols,
+                    void* stream);
+
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode, fa_bwd / fa_bwd_f32 and
+ * fa_softmax_rows (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would
+ * return. */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, const void* dq, const void* dk,
                     const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
@@ -166,6 +187,8 @@ int fa_validate_decode(const void* q, const void* k, const void* v, const void* 
                        const float* lse, int64_t B, int64_t h, int64_t Tk, int64_t d_head,
                        float scale, int64_t num_splits, const void* workspace,
                        size_t workspace_bytes);
+int fa_validate_softmax(const float* x, const float* y, const float* lse, int64_t rows,
+                        int64_t cols);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -1,4 +1,5 @@
-"""MI355X-native IO-aware attention: fused attention forward, split-KV decode and backward.
+"""MI355X-native IO-aware attention: fused attention forward, split-KV decode, backward, and the
+one-pass row softmax.
 
 A thin binding over the C ABI of ``include/fa.h`` (``libfa_mi355x.so``).  The functions carry the
 same names as the C entry points and only marshal arguments: torch supplies device memory and the
@@ -18,7 +19,8 @@ from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR
 
 __all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
-           "fa_validate_bwd", "fa_status_str", "fa_last_hip_error", "FaError", "LIB_PATH"]
+           "fa_validate_bwd", "fa_softmax_rows", "fa_validate_softmax", "fa_status_str",
+           "fa_last_hip_error", "FaError", "LIB_PATH"]
 
 
 class FaError(RuntimeError):
@@ -214,6 +216,38 @@ def fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr,
     return int(_lib.lib.fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr,
                                         dk_ptr, dv_ptr, B, h, Tq, Tk, d_head, int(causal),
                                         float(scale), ws_ptr, ws_bytes))
+
+
+def fa_softmax_rows(x, *, y=None, lse=None, with_lse: bool = False, stream=None):
+    """Row softmax of a contiguous [rows, cols] fp32 GPU tensor -> (y, lse or None).
+
+    ``y`` (and, with ``with_lse`` or a given ``lse``, the [rows] fp32 log-sum-exp) are allocated
+    with ``torch.empty`` unless given.
+    """
+    _check_tensor("x", x, torch.float32, 2)
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    _check_tensor("y", y, torch.float32, 2)
+    if tuple(y.shape) != (rows, cols) or y.device != x.device:
+        raise ValueError("y must match x in shape and device")
+    if lse is None and with_lse:
+        lse = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, 1)
+        if lse.shape[0] != rows:
+            raise ValueError("lse must have one entry per row")
+    st = _lib.lib.fa_softmax_rows(x.data_ptr(), y.data_ptr(),
+                                  None if lse is None else lse.data_ptr(), rows, cols,
+                                  _stream_handle(stream, x.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return y, lse
+
+
+def fa_validate_softmax(x_ptr, y_ptr, lse_ptr, rows, cols):
+    """Host-only argument check of fa_softmax_rows (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_softmax(x_ptr, y_ptr, lse_ptr, rows, cols))
 
 
 def fa_validate_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head, causal, scale):

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libfa_mi355x.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m io_aware_attention_fa_amd.build` "
+        f"{LIB_PATH} is not built; run `python io_aware_attention_fa_amd/build.py` "
         "(or __graft_entry__.build()) first. There is no CPU fallback.")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -36,6 +36,8 @@ SIGNATURES = {
                           _i64, _int, _f32, _vp, _size, _vp]),
     "fa_validate_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                _i64, _i64, _int, _f32, _vp, _size]),
+    "fa_softmax_rows": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "fa_validate_softmax": (_int, [_vp, _vp, _vp, _i64, _i64]),
     "fa_status_str": (ctypes.c_char_p, [_int]),
     "fa_last_hip_error": (_int, []),
 }

@@ -1,7 +1,9 @@
 """Build the C-ABI library libfa_mi355x.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m io_aware_attention_fa_amd.build`` (or ``build_library()``).  Every call
-compiles from source; objects go to ``_build/`` and the library next to this file.
+Usage: ``python io_aware_attention_fa_amd/build.py`` (or ``__graft_entry__.build()``).  Run it as
+a file, not as ``-m io_aware_attention_fa_amd.build``: importing the package loads the library,
+which fails while it is missing or older than its header.  Every call compiles from source;
+objects go to ``_build/`` and the library next to this file.
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_mi355x.so"
 
 SOURCES = ["fa_validate.cpp", "fa_host.cpp", "fa_fwd_kernel.hip", "fa_decode_kernel.hip",
-           "fa_bwd_kernel.hip"]
+           "fa_bwd_kernel.hip", "fa_softmax_kernel.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are kept out of every kernel.

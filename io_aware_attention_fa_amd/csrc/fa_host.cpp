@@ -93,4 +93,13 @@ extern "C" int fa_bwd_f32(const void* q, const void* k, const void* v, const voi
                     workspace, workspace_bytes, stream, true);
 }
 
+extern "C" int fa_softmax_rows(const float* x, float* y, float* lse, int64_t rows, int64_t cols,
+                               void* stream) {
+  const int st = fa_validate_softmax(x, y, lse, rows, cols);
+  if (st != FA_OK) return st;
+  fa::SoftmaxLaunch a;
+  a.x = x; a.y = y; a.lse = lse; a.rows = rows; a.cols = cols;
+  return map_hip(fa::launch_softmax(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int fa_last_hip_error(void) { return g_last_hip_error; }

@@ -47,8 +47,16 @@ struct BwdLaunch {
   float scale;
 };
 
+struct SoftmaxLaunch {
+  const float* x;
+  float* y;
+  float* lse;   // may be null
+  int64_t rows, cols;
+};
+
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);
+hipError_t launch_softmax(const SoftmaxLaunch& a, hipStream_t stream);
 
 }  // namespace fa

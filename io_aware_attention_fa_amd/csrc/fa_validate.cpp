@@ -103,6 +103,16 @@ extern "C" int fa_validate_bwd(const void* q, const void* k, const void* v, cons
   return FA_OK;
 }
 
+extern "C" int fa_validate_softmax(const float* x, const float* y, const float* lse, int64_t rows,
+                                   int64_t cols) {
+  if (!x || !y) return FA_ERR_NULL;
+  if (rows < 1 || cols < 1 || cols > INT32_MAX) return FA_ERR_SHAPE;
+  // four rows per workgroup; the grid's x extent is below 2^31
+  if ((rows + 3) / 4 > INT32_MAX) return FA_ERR_SHAPE;
+  if (!aligned(x, 4) || !aligned(y, 4) || (lse && !aligned(lse, 4))) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

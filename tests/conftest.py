@@ -23,7 +23,11 @@ def _gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def fa_lib():
     """The built C-ABI library (built in-tree first if it is missing)."""
-    from io_aware_attention_fa_amd import build as fabuild
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "fa_amd_build", os.path.join(ROOT, "io_aware_attention_fa_amd", "build.py"))
+    fabuild = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(fabuild)   # by path: the package import would load the library
     if not os.path.exists(fabuild.library_path()):
         fabuild.build_library()
     import io_aware_attention_fa_amd as fa

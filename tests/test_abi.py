@@ -169,3 +169,22 @@ def test_invalid_bwd_call_touches_nothing(fa_lib):
                              ws.nbytes, None)
     assert st == 4
     assert np.all(out == 0x7FC1) and np.all(ws == 7)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, 0, 4, 4096), 0), ((P, P, P, 4, 4096), 0),
+    ((0, P, 0, 4, 4096), 1), ((P, 0, 0, 4, 4096), 1),
+    ((P, P, 0, 0, 4096), 2), ((P, P, 0, 4, 0), 2), ((P, P, 0, 4, 2**31), 2),
+    ((P + 2, P, 0, 4, 4096), 5), ((P, P, P + 1, 4, 4096), 5), ((P + 4, P + 8, 0, 3, 7), 0),
+])
+def test_validate_softmax(fa_lib, args, code):
+    assert fa_lib.fa_validate_softmax(*args) == code
+
+
+def test_invalid_softmax_call_touches_nothing(fa_lib):
+    from io_aware_attention_fa_amd import _lib
+    x = np.zeros(64, dtype=np.float32)
+    y = np.full(64, 7.0, dtype=np.float32)
+    st = _lib.lib.fa_softmax_rows(ctypes.c_void_p(x.ctypes.data), ctypes.c_void_p(y.ctypes.data),
+                                  None, 0, 64, None)
+    assert st == 2 and np.all(y == 7.0)
