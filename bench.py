@@ -14,6 +14,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
   backward = the attention backward (dQ, dK, dV) on the forward workload, timed separately
              after the steps (not part of ms_per_step): TFLOP/s at 2.5x the forward's FLOPs,
              against the MFMA peak, with its own bounded CPU-oracle sample
+  softmax  = the one-pass row softmax on a 4096 x 4096 fp32 matrix, timed separately: HBM GB/s
+             (one read and one write of the matrix) against the HBM peak
 """
 from __future__ import annotations
 
@@ -176,17 +178,76 @@ def measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse):
     return res
 
 
+def time_calls(torch, fn, warmup, steps):
+    """Average, min and median milliseconds of `steps` calls of fn, each bracketed by HIP events
+    on the current stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return sum(t) / steps, min(t), sorted(t)[steps // 2]
+
+
+def measure_softmax(args, fa, si, torch):
+    """The row softmax on the pages' 4096 x 4096 fp32 matrix (seeded N(0,1) rows)."""
+    from io_aware_attention_fa_amd import costmodel as cm
+    rows, cols = si.SOFTMAX_WORKLOAD
+    x = torch.from_numpy(si.softmax_rows_input(rows, cols, seed=0)).cuda()
+    y = torch.empty_like(x)
+    K = 100
+    ms, mn, med = time_calls(torch, lambda: fa.fa_softmax_rows(x, y=y), 10, K)
+    nbytes = 2.0 * rows * cols * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    peak = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
+    eprint(f"[bench] softmax {rows}x{cols} avg {ms * 1e3:.1f} us  {gbs:.0f} GB/s  "
+           f"{100 * gbs / peak:.1f}% of HBM peak")
+    res = {"metric": "row softmax HBM GB/s (one read + one write of the fp32 matrix)",
+           "value": gbs, "unit": "GB/s", "steps": K, "warmup": 10, "avg_ms": ms, "min_ms": mn,
+           "median_ms": med,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak, "unit": "GB/s",
+                        "frac": gbs / peak,
+                        "traffic": traffic_from_profiles(
+                            f"fa_softmax_reg_kernel__softmax_{rows}x{cols}")},
+           "config": {"rows": rows, "cols": cols, "dtype": "f32", "alg_bytes": nbytes}}
+    if not args.no_cpu_baseline:
+        import time as _t
+
+        import numpy as np  # noqa: F401
+        from oracle import softmax_ref as sref
+        n, el = 0, 0.0
+        while n == 0 or (el < min(args.cpu_seconds, 5.0) and n < rows):
+            xs = si.softmax_rows_input(256, cols, seed=0, row0=n)
+            t0 = _t.perf_counter()
+            sref.softmax_rows(xs)
+            el += _t.perf_counter() - t0
+            n += 256
+        res["cpu_baseline"] = {"value": 2.0 * n * cols * 4 / el / 1e9, "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n} rows of the {rows}x{cols} matrix, {el:.2f} s of "
+                                         "fp64 numpy (bytes counted as fp32 read + write)"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax"], default=None,
                     help="run one half of the step (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separately timed backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the separately timed softmax measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
@@ -213,9 +274,21 @@ def main():
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
     do_backward = args.only == "backward" or (args.only is None and not args.no_backward)
+    do_softmax = args.only == "softmax" or (args.only is None and not args.no_extras)
     wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
 
     t0 = time.perf_counter()
+    if args.only == "softmax":
+        sm = measure_softmax(args, fa, si, torch)
+        out = {"metric": sm["metric"], "value": sm["value"], "unit": sm["unit"],
+               "n_gpus": 1, "steps": sm["steps"], "warmup": sm["warmup"],
+               "ms_per_step": sm["avg_ms"], "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+               "roofline": sm["roofline"], "config": {"workload": "softmax_rows_4096x4096_f32"},
+               "cpu_baseline": sm.get("cpu_baseline")}
+        print(json.dumps(out), flush=True)
+        return
+
     if do_prefill or do_backward:
         q, k, v = si.make_inputs(wp, seed=0)
         pq, pk, pv = upload(q), upload(k), upload(v)
@@ -334,6 +407,8 @@ def main():
         out["cpu_baseline"] = None
     if do_backward:
         out["backward"] = measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse)
+    if do_softmax:
+        out["softmax"] = measure_softmax(args, fa, si, torch)
     print(json.dumps(out), flush=True)
 
 

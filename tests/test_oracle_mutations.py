@@ -95,3 +95,33 @@ def test_softmax_mutant_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_softmax.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
+
+
+ELEMENTWISE_SRC = os.path.join(ROOT, "oracle", "elementwise_ref.py")
+ELEMENTWISE_MUTANTS = {
+    "gelu cubic coefficient": ("GELU_A = 0.044715", "GELU_A = 0.04715"),
+    "gelu without the half": ("return 0.5 * x * (1.0 + np.tanh(", "return x * (1.0 + np.tanh("),
+    "philox multipliers swapped": ("p0 = m0 * c0", "p0 = m1 * c0"),
+    "philox key never bumped": ("k0 = (k0 + np.uint64(PHILOX_W0)) & mask", "k0 = k0"),
+    "philox output order": ("c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0",
+                            "c0, c1, c2, c3 = hi0 ^ c1 ^ k0, lo1, hi1 ^ c3 ^ k1, lo0"),
+    "dropout without the rescale": ("np.where(keep, g / (1.0 - p), 0.0)", "np.where(keep, g, 0.0)"),
+    "dropout decision inverted": ("keep = words >= np.uint32(dropout_threshold(p))",
+                                  "keep = words < np.uint32(dropout_threshold(p))"),
+    "words indexed by block": ("return words[np.arange(n), (e % np.uint64(4)).astype(np.int64)]",
+                               "return words[np.arange(n), 0]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ELEMENTWISE_MUTANTS))
+def test_elementwise_mutant_is_caught(name, tmp_path):
+    old, new = ELEMENTWISE_MUTANTS[name]
+    src = open(ELEMENTWISE_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    path = tmp_path / "mutant_elementwise.py"
+    path.write_text(src.replace(old, new))
+    env = dict(os.environ, FA_ORACLE_ELEMENTWISE_MUTANT_FILE=str(path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_elementwise.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout[-2000:]}"
