@@ -53,7 +53,8 @@ enum {
   FA_ERR_SCALE = 6,            /* scale is not finite, or causal is not 0 / 1                   */
   FA_ERR_SPLITS = 7,           /* num_splits outside [1, min(Tk, FA_MAX_SPLITS)]                */
   FA_ERR_WORKSPACE = 8,        /* decode workspace NULL, misaligned or smaller than required     */
-  FA_ERR_HIP = 9               /* a HIP launch failed; see fa_last_hip_error()                  */
+  FA_ERR_HIP = 9,              /* a HIP launch failed; see fa_last_hip_error()                  */
+  FA_ERR_PROB = 10             /* a dropout probability outside [0, 1)                          */
 };
 
 /* Largest per-head tensor the kernels address with 32-bit byte offsets: T * d_head * 2 bytes
@@ -172,8 +173,37 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
 int fa_softmax_rows(const float* x, float* y, float* lse, int64_t rows, int64_t cols,
                     void* stream);
 
-/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode, fa_bwd / fa_bwd_f32 and
- * fa_softmax_rows (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would
+/*
+ * fa_gelu_f32, fa_gelu_bf16 -- y = gelu(x) elementwise over n contiguous values, in one pass over
+ *   HBM (one read, one write per element).  GELU in the tanh form of page "Chapter 10 Writing and
+ *   Benchmarking Custom Kernels", section 10.2.1 (the GeLU case study, whose workload is 64M fp32
+ *   values): gelu(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), computed in fp32 as
+ *   x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3))).  fa_gelu_bf16 reads and writes bf16 (round
+ *   to nearest even), computing in fp32.
+ *   Preconditions: n >= 1; x, y 16-byte aligned; y equal to x or not overlapping it.
+ */
+int fa_gelu_f32(const float* x, float* y, int64_t n, void* stream);
+int fa_gelu_bf16(const void* x, void* y, int64_t n, void* stream);
+
+/*
+ * fa_bias_gelu_dropout_bf16 -- the fused chain y = dropout(gelu(x + bias)) over a row-major
+ *   [rows][cols] bf16 activation with one bf16 bias per column (page "Fusion and IO-aware
+ *   kernels", "The idea in one minute": bias add, GELU and dropout as one kernel that reads x once
+ *   and writes y once).  Arithmetic in fp32, y rounded to bf16 (round to nearest even).
+ *   Dropout: element e = row * cols + col draws word e % 4 of Philox4x32-10 (Salmon et al.,
+ *   "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter (e / 4 low 32 bits,
+ *   e / 4 high 32 bits, offset low, offset high) and key (seed low, seed high); it is dropped
+ *   (y = 0) iff that word is below floor(p * 2^32), else y = gelu(x + bias) * (1 / (1 - p)) with
+ *   the factor rounded to fp32.  The same (seed, offset) reproduces the same mask bit for bit.
+ *   Preconditions: rows, cols >= 1; 0 <= p < 1 (else FA_ERR_PROB); x, bias, y 2-byte aligned
+ *   (16-byte aligned with cols % 8 == 0 and rows <= 65535 takes the vector path); y equal to x
+ *   or not overlapping it.
+ */
+int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t rows,
+                              int64_t cols, float p, uint64_t seed, uint64_t offset, void* stream);
+
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode, fa_bwd / fa_bwd_f32,
+ * fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16 (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would
  * return. */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, const void* dq, const void* dk,
@@ -189,6 +219,9 @@ int fa_validate_decode(const void* q, const void* k, const void* v, const void* 
                        size_t workspace_bytes);
 int fa_validate_softmax(const float* x, const float* y, const float* lse, int64_t rows,
                         int64_t cols);
+int fa_validate_gelu(const void* x, const void* y, int64_t n);
+int fa_validate_bias_gelu_dropout(const void* x, const void* bias, const void* y, int64_t rows,
+                                  int64_t cols, float p);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -1,5 +1,5 @@
-"""MI355X-native IO-aware attention: fused attention forward, split-KV decode, backward, and the
-one-pass row softmax.
+"""MI355X-native IO-aware attention: fused attention forward, split-KV decode, backward, the
+one-pass row softmax, and the fused GELU / bias-GELU-dropout elementwise chains.
 
 A thin binding over the C ABI of ``include/fa.h`` (``libfa_mi355x.so``).  The functions carry the
 same names as the C entry points and only marshal arguments: torch supplies device memory and the
@@ -14,13 +14,15 @@ import torch
 
 from . import _lib
 from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR_HIP,  # noqa: F401
-                   FA_ERR_NULL, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS, FA_ERR_WORKSPACE,
-                   FA_OK, LIB_PATH)
+                   FA_ERR_NULL, FA_ERR_PROB, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS,
+                   FA_ERR_WORKSPACE, FA_OK, LIB_PATH)
 
 __all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
-           "fa_validate_bwd", "fa_softmax_rows", "fa_validate_softmax", "fa_status_str",
-           "fa_last_hip_error", "FaError", "LIB_PATH"]
+           "fa_validate_bwd", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
+           "fa_gelu_bf16", "fa_bias_gelu_dropout_bf16", "fa_validate_gelu",
+           "fa_validate_bias_gelu_dropout", "fa_status_str", "fa_last_hip_error", "FaError",
+           "LIB_PATH"]
 
 
 class FaError(RuntimeError):
@@ -248,6 +250,68 @@ def fa_softmax_rows(x, *, y=None, lse=None, with_lse: bool = False, stream=None)
 def fa_validate_softmax(x_ptr, y_ptr, lse_ptr, rows, cols):
     """Host-only argument check of fa_softmax_rows (raw integer addresses)."""
     return int(_lib.lib.fa_validate_softmax(x_ptr, y_ptr, lse_ptr, rows, cols))
+
+
+def _gelu(entry, dtype, x, y, stream):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != dtype:
+        raise ValueError(f"x must be a {dtype} GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if y is None:
+        y = torch.empty_like(x)
+    if (not isinstance(y, torch.Tensor) or y.dtype != dtype or y.device != x.device or
+            y.shape != x.shape or not y.is_contiguous()):
+        raise ValueError("y must be a contiguous tensor like x")
+    st = entry(x.data_ptr(), y.data_ptr(), x.numel(), _stream_handle(stream, x.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return y
+
+
+def fa_gelu_f32(x, *, y=None, stream=None):
+    """GELU (tanh form) of a contiguous fp32 GPU tensor of any shape, one pass over HBM."""
+    return _gelu(_lib.lib.fa_gelu_f32, torch.float32, x, y, stream)
+
+
+def fa_gelu_bf16(x, *, y=None, stream=None):
+    """GELU (tanh form) of a contiguous bf16 GPU tensor, fp32 arithmetic, bf16 output."""
+    return _gelu(_lib.lib.fa_gelu_bf16, torch.bfloat16, x, y, stream)
+
+
+def fa_bias_gelu_dropout_bf16(x, bias, *, p: float, seed: int, offset: int = 0, y=None,
+                              stream=None):
+    """y = dropout(gelu(x + bias)) for a contiguous [rows, cols] bf16 tensor and a [cols] bias.
+
+    The mask comes from Philox4x32-10 at (seed, offset) as the C header specifies.
+    """
+    _check_tensor("x", x, torch.bfloat16, 2)
+    _check_tensor("bias", bias, torch.bfloat16, 1)
+    rows, cols = x.shape
+    if bias.shape[0] != cols or bias.device != x.device:
+        raise ValueError("bias must have one entry per column, on x's device")
+    if y is None:
+        y = torch.empty_like(x)
+    _check_tensor("y", y, torch.bfloat16, 2)
+    if tuple(y.shape) != (rows, cols):
+        raise ValueError("y must match x")
+    st = _lib.lib.fa_bias_gelu_dropout_bf16(x.data_ptr(), bias.data_ptr(), y.data_ptr(), rows,
+                                            cols, float(p), int(seed) & (2**64 - 1),
+                                            int(offset) & (2**64 - 1),
+                                            _stream_handle(stream, x.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return y
+
+
+def fa_validate_gelu(x_ptr, y_ptr, n):
+    """Host-only argument check of fa_gelu_f32 / fa_gelu_bf16 (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_gelu(x_ptr, y_ptr, n))
+
+
+def fa_validate_bias_gelu_dropout(x_ptr, bias_ptr, y_ptr, rows, cols, p):
+    """Host-only argument check of fa_bias_gelu_dropout_bf16 (raw integer addresses)."""
+    return int(_lib.lib.fa_validate_bias_gelu_dropout(x_ptr, bias_ptr, y_ptr, rows, cols,
+                                                      float(p)))
 
 
 def fa_validate_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head, causal, scale):

@@ -38,6 +38,12 @@ SIGNATURES = {
                                _i64, _i64, _int, _f32, _vp, _size]),
     "fa_softmax_rows": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "fa_validate_softmax": (_int, [_vp, _vp, _vp, _i64, _i64]),
+    "fa_gelu_f32": (_int, [_vp, _vp, _i64, _vp]),
+    "fa_gelu_bf16": (_int, [_vp, _vp, _i64, _vp]),
+    "fa_bias_gelu_dropout_bf16": (_int, [_vp, _vp, _vp, _i64, _i64, _f32, ctypes.c_uint64,
+                                         ctypes.c_uint64, _vp]),
+    "fa_validate_gelu": (_int, [_vp, _vp, _i64]),
+    "fa_validate_bias_gelu_dropout": (_int, [_vp, _vp, _vp, _i64, _i64, _f32]),
     "fa_status_str": (ctypes.c_char_p, [_int]),
     "fa_last_hip_error": (_int, []),
 }
@@ -57,3 +63,4 @@ FA_ERR_SCALE = 6
 FA_ERR_SPLITS = 7
 FA_ERR_WORKSPACE = 8
 FA_ERR_HIP = 9
+FA_ERR_PROB = 10

@@ -1,6 +1,8 @@
 // C-ABI entry points: validate on the host, then enqueue the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "fa.h"
 #include "fa_internal.hpp"
 
@@ -100,6 +102,37 @@ extern "C" int fa_softmax_rows(const float* x, float* y, float* lse, int64_t row
   fa::SoftmaxLaunch a;
   a.x = x; a.y = y; a.lse = lse; a.rows = rows; a.cols = cols;
   return map_hip(fa::launch_softmax(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa_gelu_f32(const float* x, float* y, int64_t n, void* stream) {
+  const int st = fa_validate_gelu(x, y, n);
+  if (st != FA_OK) return st;
+  fa::GeluLaunch a;
+  a.x = x; a.y = y; a.n = n; a.bf16 = false;
+  return map_hip(fa::launch_gelu(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa_gelu_bf16(const void* x, void* y, int64_t n, void* stream) {
+  const int st = fa_validate_gelu(x, y, n);
+  if (st != FA_OK) return st;
+  fa::GeluLaunch a;
+  a.x = x; a.y = y; a.n = n; a.bf16 = true;
+  return map_hip(fa::launch_gelu(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t rows,
+                                         int64_t cols, float p, uint64_t seed, uint64_t offset,
+                                         void* stream) {
+  const int st = fa_validate_bias_gelu_dropout(x, bias, y, rows, cols, p);
+  if (st != FA_OK) return st;
+  fa::DropoutLaunch a;
+  a.x = x; a.bias = bias; a.y = y; a.rows = rows; a.cols = cols;
+  // drop iff word < floor(p * 2^32); kept values scaled by 1 / (1 - p)
+  const double t = std::floor(static_cast<double>(p) * 4294967296.0);
+  a.threshold = t >= 4294967295.0 ? 0xffffffffu : static_cast<uint32_t>(t);
+  a.scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
+  a.seed = seed; a.offset = offset;
+  return map_hip(fa::launch_bias_gelu_dropout(a, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int fa_last_hip_error(void) { return g_last_hip_error; }

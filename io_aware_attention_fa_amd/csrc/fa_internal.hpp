@@ -54,9 +54,28 @@ struct SoftmaxLaunch {
   int64_t rows, cols;
 };
 
+struct GeluLaunch {
+  const void* x;
+  void* y;
+  int64_t n;
+  bool bf16;
+};
+
+struct DropoutLaunch {
+  const void* x;
+  const void* bias;
+  void* y;
+  int64_t rows, cols;
+  uint32_t threshold;   // drop iff the element's generator word is below it
+  float scale;          // 1 / (1 - p)
+  uint64_t seed, offset;
+};
+
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);
 hipError_t launch_softmax(const SoftmaxLaunch& a, hipStream_t stream);
+hipError_t launch_gelu(const GeluLaunch& a, hipStream_t stream);
+hipError_t launch_bias_gelu_dropout(const DropoutLaunch& a, hipStream_t stream);
 
 }  // namespace fa

@@ -113,6 +113,22 @@ extern "C" int fa_validate_softmax(const float* x, const float* y, const float* 
   return FA_OK;
 }
 
+extern "C" int fa_validate_gelu(const void* x, const void* y, int64_t n) {
+  if (!x || !y) return FA_ERR_NULL;
+  if (n < 1) return FA_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+extern "C" int fa_validate_bias_gelu_dropout(const void* x, const void* bias, const void* y,
+                                             int64_t rows, int64_t cols, float p) {
+  if (!x || !bias || !y) return FA_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows > INT64_MAX / cols / 2) return FA_ERR_SHAPE;
+  if (!aligned(x, 2) || !aligned(bias, 2) || !aligned(y, 2)) return FA_ERR_ALIGN;
+  if (!(p >= 0.0f && p < 1.0f)) return FA_ERR_PROB;   // also rejects NaN
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -125,6 +141,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: num_splits must be in [1, min(Tk, FA_MAX_SPLITS)]";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, misaligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed (see fa_last_hip_error)";
+    case FA_ERR_PROB: return "FA_ERR_PROB: the dropout probability must be in [0, 1)";
     default: return "unknown fa status code";
   }
 }

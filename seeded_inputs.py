@@ -11,6 +11,9 @@ Generator (fixed so that any single head can be regenerated on its own):
     gradient dO of the backward workloads is 4 (standard normal like the others);
   * the row-softmax workload's fp32 matrix is drawn the same way, row by row, from stream
     ``[seed, 5, row]`` (float32 standard normal, not rounded to bf16);
+  * the GELU workload's flat fp32 vector is stream ``[seed, 6]``; the bias-GELU-dropout
+    activation [rows][cols] is stream ``[seed, 7]`` and its per-column bias ``[seed, 8]``, both
+    rounded to bf16;
   * float32 -> bfloat16 is round-to-nearest-even on the bit pattern (inputs are finite);
   * the long-context workload scales a Bernoulli(1%) subset of key vectors by 8 (a power of two,
     so the scaling is exact in bf16); the subset of head (b, h) is ``random(T) < 0.01`` drawn from
@@ -28,6 +31,7 @@ from dataclasses import dataclass
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_KEY_SPIKES, TENSOR_DO, TENSOR_SOFTMAX = 0, 1, 2, 3, 4, 5
+TENSOR_ELEMENTWISE, TENSOR_ACTIVATION, TENSOR_BIAS = 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -159,6 +163,23 @@ def softmax_rows_input(rows: int, cols: int, seed: int = 0, row0: int = 0) -> np
         rng = np.random.default_rng([seed, TENSOR_SOFTMAX, row0 + r])
         out[r] = rng.standard_normal(cols, dtype=np.float32)
     return out
+
+
+GELU_WORKLOAD_N = 64_000_000          # fp32 elements (the pages' GeLU case study)
+DROPOUT_WORKLOAD = (4096, 8192, 0.1)  # rows, cols, p: the pages' 4096 x 8192 bf16 activation
+
+
+def elementwise_input(n: int, seed: int = 0) -> np.ndarray:
+    """The flat fp32 GELU input (standard normal)."""
+    return np.random.default_rng([seed, TENSOR_ELEMENTWISE]).standard_normal(n, dtype=np.float32)
+
+
+def activation_input(rows: int, cols: int, seed: int = 0):
+    """(x [rows][cols], bias [cols]) as bf16 bit patterns for the bias-GELU-dropout chain."""
+    x = np.random.default_rng([seed, TENSOR_ACTIVATION]).standard_normal(rows * cols,
+                                                                         dtype=np.float32)
+    b = np.random.default_rng([seed, TENSOR_BIAS]).standard_normal(cols, dtype=np.float32)
+    return rne_bf16_bits(x).reshape(rows, cols), rne_bf16_bits(b)
 
 
 def custom_workload(B, h, Tq, Tk, d, causal, name="custom", **kw) -> Workload:

@@ -44,7 +44,7 @@ def test_binding_covers_every_declared_function(fa_lib):
 
 def test_status_strings(fa_lib):
     seen = set()
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa_lib.fa_status_str(code)
         assert s and s not in seen
         seen.add(s)
@@ -188,3 +188,22 @@ def test_invalid_softmax_call_touches_nothing(fa_lib):
     st = _lib.lib.fa_softmax_rows(ctypes.c_void_p(x.ctypes.data), ctypes.c_void_p(y.ctypes.data),
                                   None, 0, 64, None)
     assert st == 2 and np.all(y == 7.0)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, 1), 0), ((P, P, 2**40), 0), ((0, P, 5), 1), ((P, 0, 5), 1), ((P, P, 0), 2),
+    ((P + 4, P, 5), 5), ((P, P + 8, 5), 5),
+])
+def test_validate_gelu(fa_lib, args, code):
+    assert fa_lib.fa_validate_gelu(*args) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, P, 4096, 8192, 0.1), 0), ((P, P, P, 3, 7, 0.0), 0), ((P + 2, P, P + 2, 3, 7, 0.5), 0),
+    ((0, P, P, 4, 4, 0.1), 1), ((P, 0, P, 4, 4, 0.1), 1),
+    ((P, P, P, 0, 4, 0.1), 2), ((P, P, P, 4, 0, 0.1), 2), ((P, P, P, 2**40, 2**40, 0.1), 2),
+    ((P + 1, P, P, 4, 4, 0.1), 5),
+    ((P, P, P, 4, 4, 1.0), 10), ((P, P, P, 4, 4, -0.1), 10), ((P, P, P, 4, 4, math.nan), 10),
+])
+def test_validate_bias_gelu_dropout(fa_lib, args, code):
+    assert fa_lib.fa_validate_bias_gelu_dropout(*args) == code
