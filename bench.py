@@ -16,6 +16,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
              against the MFMA peak, with its own bounded CPU-oracle sample
   softmax  = the one-pass row softmax on a 4096 x 4096 fp32 matrix, timed separately: HBM GB/s
              (one read and one write of the matrix) against the HBM peak
+  gelu, bias_gelu_dropout = the fused elementwise chains on the pages' workloads (64M fp32
+             values; a 4096 x 8192 bf16 activation with p = 0.1), timed separately: HBM GB/s
 """
 from __future__ import annotations
 
@@ -179,20 +181,19 @@ def measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse):
 
 
 def time_calls(torch, fn, warmup, steps):
-    """Average, min and median milliseconds of `steps` calls of fn, each bracketed by HIP events
-    on the current stream (the stream the library launches on)."""
+    """Average milliseconds per call of `steps` back-to-back calls of fn, between two HIP events
+    on the current stream (the stream the library launches on).  For kernels of tens of
+    microseconds, one event pair per call would add its own overhead to every call."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:
-        a.record()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    t = [a.elapsed_time(b) for a, b in ev]
-    return sum(t) / steps, min(t), sorted(t)[steps // 2]
+    return a.elapsed_time(b) / steps
 
 
 def measure_softmax(args, fa, si, torch):
@@ -201,16 +202,15 @@ def measure_softmax(args, fa, si, torch):
     rows, cols = si.SOFTMAX_WORKLOAD
     x = torch.from_numpy(si.softmax_rows_input(rows, cols, seed=0)).cuda()
     y = torch.empty_like(x)
-    K = 100
-    ms, mn, med = time_calls(torch, lambda: fa.fa_softmax_rows(x, y=y), 10, K)
+    K = args.extra_steps or 100
+    ms = time_calls(torch, lambda: fa.fa_softmax_rows(x, y=y), 3, K)
     nbytes = 2.0 * rows * cols * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     peak = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
     eprint(f"[bench] softmax {rows}x{cols} avg {ms * 1e3:.1f} us  {gbs:.0f} GB/s  "
            f"{100 * gbs / peak:.1f}% of HBM peak")
     res = {"metric": "row softmax HBM GB/s (one read + one write of the fp32 matrix)",
-           "value": gbs, "unit": "GB/s", "steps": K, "warmup": 10, "avg_ms": ms, "min_ms": mn,
-           "median_ms": med,
+           "value": gbs, "unit": "GB/s", "steps": K, "warmup": 3, "avg_ms": ms,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak, "unit": "GB/s",
                         "frac": gbs / peak,
                         "traffic": traffic_from_profiles(
@@ -235,19 +235,90 @@ def measure_softmax(args, fa, si, torch):
     return res
 
 
+def measure_elementwise(args, fa, si, torch):
+    """GELU on the pages' 64M fp32 values and bias-GELU-dropout on a 4096 x 8192 bf16
+    activation (p = 0.1); each HBM GB/s counts one read and one write of the tensor."""
+    import numpy as np
+    from io_aware_attention_fa_amd import costmodel as cm
+    peak = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
+    res = {}
+    n = si.GELU_WORKLOAD_N
+    xh = si.elementwise_input(n, seed=0)
+    x = torch.from_numpy(xh).cuda()
+    y = torch.empty_like(x)
+    K = args.extra_steps or 50
+    ms = time_calls(torch, lambda: fa.fa_gelu_f32(x, y=y), 5, K)
+    nbytes = 8.0 * n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    eprint(f"[bench] gelu f32 n={n} avg {ms * 1e3:.1f} us  {gbs:.0f} GB/s  "
+           f"{100 * gbs / peak:.1f}% of HBM peak")
+    g = {"metric": "GELU (tanh form) HBM GB/s, one read + one write of 64M fp32 values",
+         "value": gbs, "unit": "GB/s", "steps": K, "warmup": 5, "avg_ms": ms,
+         "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak, "unit": "GB/s",
+                      "frac": gbs / peak,
+                      "traffic": traffic_from_profiles("fa_gelu_f32_kernel__gelu_64M_f32")},
+         "config": {"n": n, "dtype": "f32", "alg_bytes": nbytes}}
+    if not args.no_cpu_baseline:
+        from oracle import elementwise_ref as eref
+        m = 4_000_000
+        t0 = time.perf_counter()
+        eref.gelu_tanh(xh[:m])
+        el = time.perf_counter() - t0
+        g["cpu_baseline"] = {"value": 8.0 * m / el / 1e9, "unit": "GB/s", "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"the first {m} of the {n} values, {el:.2f} s of fp64 "
+                                       "numpy (bytes counted as fp32 read + write)"}
+    res["gelu"] = g
+    del x, y
+    rows, cols, p = si.DROPOUT_WORKLOAD
+    xb, bb = si.activation_input(rows, cols, seed=0)
+    xa = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    ba = torch.from_numpy(bb.view(np.int16)).view(torch.bfloat16).cuda()
+    ya = torch.empty_like(xa)
+    ms = time_calls(torch, lambda: fa.fa_bias_gelu_dropout_bf16(xa, ba, p=p, seed=1234, y=ya), 5,
+                    K)
+    nbytes = 4.0 * rows * cols
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    eprint(f"[bench] bias-gelu-dropout {rows}x{cols} p={p} avg {ms * 1e3:.1f} us  {gbs:.0f} GB/s  "
+           f"{100 * gbs / peak:.1f}% of HBM peak")
+    d = {"metric": "bias-GELU-dropout HBM GB/s, one read + one write of the bf16 activation",
+         "value": gbs, "unit": "GB/s", "steps": K, "warmup": 5, "avg_ms": ms,
+         "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak, "unit": "GB/s",
+                      "frac": gbs / peak,
+                      "traffic": traffic_from_profiles(
+                          f"fa_bias_gelu_dropout_vec_kernel__dropout_{rows}x{cols}_bf16")},
+         "config": {"rows": rows, "cols": cols, "p": p, "dtype": "bf16", "alg_bytes": nbytes}}
+    if not args.no_cpu_baseline:
+        from oracle import elementwise_ref as eref
+        r = 64
+        t0 = time.perf_counter()
+        eref.bias_gelu_dropout(si.bf16_bits_to_f64(xb[:r]), si.bf16_bits_to_f64(bb), p, 1234, 0)
+        el = time.perf_counter() - t0
+        d["cpu_baseline"] = {"value": 4.0 * r * cols / el / 1e9, "unit": "GB/s", "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"the first {r} rows of {rows}, {el:.2f} s of fp64 numpy "
+                                       "with the Philox stream (bytes counted as bf16 read + "
+                                       "write)"}
+    res["bias_gelu_dropout"] = d
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax", "elementwise"],
+                    default=None,
                     help="run one half of the step (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separately timed backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=20)
+    ap.add_argument("--extra-steps", type=int, default=0,
+                    help="timed calls of each separately measured kernel (0: its default)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the separately timed softmax measurement")
+                    help="skip the separately timed softmax and elementwise measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
@@ -271,10 +342,21 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     eprint(f"[bench] device {props.name} CUs={props.multi_processor_count} lib={fa.LIB_PATH}")
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2**20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        eprint(f"[bench] copy probe of {n} bytes done")
+
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
     do_backward = args.only == "backward" or (args.only is None and not args.no_backward)
     do_softmax = args.only == "softmax" or (args.only is None and not args.no_extras)
+    do_elementwise = args.only == "elementwise" or (args.only is None and not args.no_extras)
     wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
 
     t0 = time.perf_counter()
@@ -286,6 +368,19 @@ def main():
                "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "roofline": sm["roofline"], "config": {"workload": "softmax_rows_4096x4096_f32"},
                "cpu_baseline": sm.get("cpu_baseline")}
+        print(json.dumps(out), flush=True)
+        return
+
+    if args.only == "elementwise":
+        ew = measure_elementwise(args, fa, si, torch)
+        g = ew["gelu"]
+        out = {"metric": g["metric"], "value": g["value"], "unit": g["unit"], "n_gpus": 1,
+               "steps": g["steps"], "warmup": g["warmup"], "ms_per_step": g["avg_ms"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+               "data": "synthetic", "roofline": g["roofline"],
+               "config": {"workload": "gelu_64M_f32 + bias_gelu_dropout_4096x8192_bf16"},
+               "cpu_baseline": g.get("cpu_baseline"),
+               "bias_gelu_dropout": ew["bias_gelu_dropout"]}
         print(json.dumps(out), flush=True)
         return
 
@@ -306,14 +401,6 @@ def main():
     torch.cuda.synchronize()
     eprint(f"[bench] inputs generated and resident in {time.perf_counter() - t0:.1f} s")
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * 2**20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        eprint(f"[bench] copy probe of {n} bytes done")
 
     if args.only == "backward":
         out = {"metric": "attention backward TFLOP/s (2.5x forward FLOPs), % MFMA peak",
@@ -409,6 +496,8 @@ def main():
         out["backward"] = measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse)
     if do_softmax:
         out["softmax"] = measure_softmax(args, fa, si, torch)
+    if do_elementwise:
+        out.update(measure_elementwise(args, fa, si, torch))
     print(json.dumps(out), flush=True)
 
 

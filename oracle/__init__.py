@@ -4,9 +4,11 @@ TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite, the ent
 check and the benchmark's CPU-baseline leg may import, call or execute anything in this package.
 The GPU library never routes through it, and it shares no code with the GPU library.
 
-Everything here is plain float64 numpy written from the definition of attention the pages give:
-materialise the score matrix, mask it, take the row softmax, multiply by V, and report the natural
-log-sum-exp of each row.  See ``attention_ref`` for the functions and their citations.
+Everything here is plain float64 numpy written from the definitions the pages give: attention
+(materialise the score matrix, mask it, take the row softmax, multiply by V, report the natural
+log-sum-exp) in ``attention_ref``; its gradients in ``attention_bwd_ref``; the row softmax and
+its running (max, sum) recurrence in ``softmax_ref``; GELU, the bias-GELU-dropout chain and its
+Philox4x32-10 dropout stream in ``elementwise_ref``.  Each module cites its passages.
 """
 from .attention_ref import (  # noqa: F401
     causal_visible,
