@@ -47,7 +47,8 @@ enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,             /* a required pointer is NULL                                    */
   FA_ERR_SHAPE = 2,            /* a size is < 1, or too large for the kernels' 32-bit offsets   */
-  FA_ERR_HEAD_DIM = 3,         /* d_head is not 64 or 128                                       */
+  FA_ERR_HEAD_DIM = 3,         /* d_head not supported (forward: multiple of 8 in [8, 128];     */
+                               /* decode and backward: 64 or 128)                               */
   FA_ERR_CAUSAL_TQ_GT_TK = 4,  /* causal with Tq > Tk (a query row would see no key)            */
   FA_ERR_ALIGN = 5,            /* a tensor pointer is not 16-byte aligned (LSE: 4-byte)          */
   FA_ERR_SCALE = 6,            /* scale is not finite, or causal is not 0 / 1                   */
@@ -58,7 +59,8 @@ enum {
 };
 
 /* Largest per-head tensor the kernels address with 32-bit byte offsets: T * d_head * 2 bytes
- * must stay below 2^31 (so T <= 8,388,607 at d_head = 128). */
+ * (strided forward: (T + 128) * row_stride * 2 bytes) must stay below 2^31 (so T <= 8,388,607 at
+ * d_head = 128, contiguous). */
 #define FA_MAX_HEAD_BYTES 2147483647LL
 /* Largest split count of the decode entry point. */
 #define FA_MAX_SPLITS 256
@@ -73,7 +75,11 @@ enum {
  *     Custom Kernels", section 10.3.1, "What You Actually Decide in Practice": causal masking and
  *     the final partial tile).  causal = 0: every key is visible.
  *   scale multiplies Q K^T before the softmax (usually 1/sqrt(d_head)); it must be finite.
- *   Preconditions: B, h, Tq, Tk >= 1; d_head in {64, 128}; causal => Tq <= Tk;
+ *   d_head: any multiple of 8 from 8 to 128.  Head dimensions other than 64 and 128 run the
+ *   64- or 128-wide kernel with the extra columns zero on chip (page "Chapter 10 Writing and
+ *   Benchmarking Custom Kernels", section 10.3.1, "What You Actually Decide in Practice": pad
+ *   d_head = 80 to 128 inside the kernel); the padding changes no result.
+ *   Preconditions: B, h, Tq, Tk >= 1; d_head as above; causal => Tq <= Tk;
  *   q, k, v, o 16-byte aligned, lse 4-byte aligned; Tq*d_head*2 and Tk*d_head*2 <= FA_MAX_HEAD_BYTES.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -88,6 +94,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_o32(const void* q, const void* k, const void* v, float* o, float* lse,
                int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
                int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_strided -- fa_fwd on strided tensors (layout variants).
+ *   Element (b, h, t, c) of q is q[b*q_strides[0] + h*q_strides[1] + t*q_strides[2] + c], and
+ *   likewise for k, v and o with their own strides (counted in elements; the last dimension is
+ *   contiguous).  For example a [B][T][h][d] tensor has strides {T*h*d, d, h*d}.  lse stays
+ *   contiguous [B][h][Tq] fp32; o is bf16.  Same computation, kernel and results as fa_fwd.
+ *   Preconditions: as fa_fwd, and for each tensor: row stride >= d_head, every stride a
+ *   non-negative multiple of 8 elements (rows stay 16-byte aligned), and
+ *   (T + 128) * row_stride * 2 <= FA_MAX_HEAD_BYTES.  o must not overlap q, k, v or lse.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                   const int64_t* q_strides, const int64_t* k_strides,
+                   const int64_t* v_strides, const int64_t* o_strides,
+                   int causal, float scale, void* stream);
 
 /*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
@@ -213,6 +235,11 @@ int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
 int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                     int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
                     int causal, float scale);
+int fa_validate_fwd_strided(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
+                            int64_t d_head, const int64_t* q_strides, const int64_t* k_strides,
+                            const int64_t* v_strides, const int64_t* o_strides, int causal,
+                            float scale);
 int fa_validate_decode(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, int64_t B, int64_t h, int64_t Tk, int64_t d_head,
                        float scale, int64_t num_splits, const void* workspace,

@@ -17,7 +17,7 @@ from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR
                    FA_ERR_NULL, FA_ERR_PROB, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS,
                    FA_ERR_WORKSPACE, FA_OK, LIB_PATH)
 
-__all__ = ["fa_fwd", "fa_fwd_o32", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
+__all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
            "fa_validate_bwd", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
            "fa_gelu_bf16", "fa_bias_gelu_dropout_bf16", "fa_validate_gelu",
@@ -118,6 +118,60 @@ def fa_fwd_o32(q, k, v, *, causal: bool, scale: float | None = None, o=None, lse
                stream=None):
     """Same kernel as :func:`fa_fwd` with an fp32 O (parity diagnostics)."""
     return _fwd(_lib.lib.fa_fwd_o32, torch.float32, q, k, v, causal, scale, o, lse, stream)
+
+
+def _strides3(name, t):
+    """(batch, head, row) element strides of a 4-D [B, h, T, d] view with a contiguous last dim."""
+    import ctypes
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D GPU tensor [B, h, T, d]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def fa_fwd_strided(q, k, v, *, causal: bool, scale: float | None = None, o=None, lse=None,
+                   stream=None):
+    """Attention forward on strided [B, h, T, d] views (e.g. ``x.transpose(1, 2)`` of a
+    [B, T, h, d] tensor): q, k, v bf16 with a contiguous last dimension -> (o, lse).
+
+    ``o`` defaults to a contiguous [B, h, Tq, d] bf16 tensor and may be any such view; ``lse`` is
+    contiguous [B, h, Tq] fp32.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a bf16 tensor")
+    B, h, Tq, d = q.shape
+    Tk = k.shape[2]
+    if tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o is None:
+        o = torch.empty((B, h, Tq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h, Tq), dtype=torch.float32, device=q.device)
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, h, Tq, d):
+        raise ValueError("o must be a bf16 [B, h, Tq, d] view")
+    _check_tensor("lse", lse, torch.float32, 3)
+    if len({t.device for t in (q, k, v, o, lse)}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = _lib.lib.fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), B, h, Tq, Tk, d, _strides3("q", q),
+                                 _strides3("k", k), _strides3("v", v), _strides3("o", o),
+                                 int(bool(causal)), scale, _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def fa_validate_fwd_strided(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk, d_head, q_strides,
+                            k_strides, v_strides, o_strides, causal, scale):
+    """Host-only argument check of fa_fwd_strided (raw addresses; strides as 3-sequences)."""
+    import ctypes
+    arr = [None if s_ is None else (ctypes.c_int64 * 3)(*s_)
+           for s_ in (q_strides, k_strides, v_strides, o_strides)]
+    return int(_lib.lib.fa_validate_fwd_strided(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tq, Tk,
+                                                d_head, *arr, int(causal), float(scale)))
 
 
 def fa_decode(q, k, v, *, num_splits: int, scale: float | None = None, o=None, lse=None,

@@ -23,6 +23,10 @@ _vp, _i64, _int, _f32, _size = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, c
 SIGNATURES = {
     "fa_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _f32, _vp]),
     "fa_fwd_o32": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _f32, _vp]),
+    "fa_fwd_strided": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+                              _vp, _vp, _int, _f32, _vp]),
+    "fa_validate_fwd_strided": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                       _vp, _vp, _vp, _vp, _int, _f32]),
     "fa_decode_workspace_size": (_size, [_i64, _i64, _i64, _i64]),
     "fa_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64, _vp, _size,
                          _vp]),

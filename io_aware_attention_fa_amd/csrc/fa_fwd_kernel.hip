@@ -78,7 +78,15 @@ struct FwdParams {
   int groups;       // workgroup groups (one per XCD); group x takes heads x, x + groups, ...
   float scale_log2;   // |scale| * log2(e), > 0
   uint32_t q_sign;    // 0x80008000 when scale < 0 (Q is negated instead), else 0
+  // Layout: element (b, h, t, c) of q is at q[b*q_b + h*q_h + t*q_t + c], likewise for k, v, o;
+  // d <= D is the true head dimension (columns d .. D - 1 are zero padding on chip).
+  int H, d;
+  int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h;
+  uint32_t q_t, k_t, v_t, o_t;
 };
+
+// A buffer offset beyond every head's range (heads are < 2^31 bytes): loads return zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
 
 template <int D>
 struct Tile {
@@ -217,10 +225,16 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return a + b;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// GEN = false: contiguous [B][h][T][D] tensors with d = D, every stride a compile-time multiple of
+// D (the layout of fa_fwd at d_head = 64 or 128); GEN = true: the strides and d of FwdParams.
+template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
   using T = Tile<D>;
+  // layout (compile-time constants in the contiguous case)
+  const int dd = GEN ? p.d : D;
+  const uint32_t q_t = GEN ? p.q_t : D, k_t = GEN ? p.k_t : D, v_t = GEN ? p.v_t : D,
+                 o_t = GEN ? p.o_t : D;
   constexpr int NS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int ND = D / 32;   // 32-row blocks of O^T
   constexpr int NK = 2 * NS, NV = 4 * ND;            // K and V^T operands per tile
@@ -266,8 +280,10 @@ void fa_fwd_kernel(FwdParams p) {
   for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
     const int r = (wave * T::LOADS_PER_WAVE + i) * T::ROWS_PER_LOAD + lane / T::CH;
     const int pc = lane % T::CH;
-    dk[i] = 2u * (uint32_t)(r * D + 8 * T::kchunk(r, pc));
-    dv[i] = 2u * (uint32_t)(r * D + 8 * T::vchunk(r, pc));
+    // (padding columns, logical chunk >= d / 8, read zeros from past the buffer's end)
+    const int ck = T::kchunk(r, pc), cv = T::vchunk(r, pc);
+    dk[i] = 8 * ck < dd ? 2u * ((uint32_t)r * k_t + 8u * (uint32_t)ck) : kPadOffset;
+    dv[i] = 8 * cv < dd ? 2u * ((uint32_t)r * v_t + 8u * (uint32_t)cv) : kPadOffset;
   }
 
   // ---- static schedule ----
@@ -307,34 +323,45 @@ void fa_fwd_kernel(FwdParams p) {
     if (it.half == 0 && p.nqb - 1 - j != j) return describe(it.pp, 1);
     return describe(it.pp + C, 0);
   };
+  // a head's element offset (rows of T elements of stride D when contiguous)
+  auto head_off = [&](int bh, int64_t sb, int64_t sh, int T_) -> int64_t {
+    if (!GEN) return (int64_t)bh * T_ * D;
+    const int b = __builtin_amdgcn_readfirstlane(bh / p.H);
+    return (int64_t)b * sb + (int64_t)(bh - b * p.H) * sh;
+  };
+  // a head's byte range: rows 0 .. T - 1 of stride st, the last one d columns wide
+  auto range = [&](int T_, uint32_t st) { return ((uint32_t)(T_ - 1) * st + (uint32_t)dd) * 2u; };
   auto k_rsrc = [&](const Item& it) {
-    return rsrc_words(p.k + (size_t)it.bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+    return rsrc_words(p.k + head_off(it.bh, p.k_b, p.k_h, p.Tk), range(p.Tk, k_t));
   };
   auto v_rsrc = [&](const Item& it) {
-    return rsrc_words(p.v + (size_t)it.bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+    return rsrc_words(p.v + head_off(it.bh, p.v_b, p.v_h, p.Tk), range(p.Tk, v_t));
   };
   // this wave's 32 query rows of an item, as the B operand fragment of S^T = K Q^T
   bf16x8_t qf[NS];
   auto load_q = [&](const Item& it) {
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(p.q + (size_t)it.bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
+        make_rsrc(p.q + head_off(it.bh, p.q_b, p.q_h, p.Tq), range(p.Tq, q_t));
     const int qrow = it.i0 + wave * 32 + r32;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4_t w = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u);
+      const int col = 16 * s + 8 * g;
+      u32x4_t w = buf_load16(
+          rq, col < dd ? ((uint32_t)qrow * q_t + (uint32_t)col) * 2u : kPadOffset);
       w ^= p.q_sign;
       qf[s] = as_bf16x8(w);
     }
   };
   // one K/V tile of an item into stage st
   auto dma = [&](u32x4_t rk, u32x4_t rv, int tile, int st) {
-    const uint32_t g0 = (uint32_t)tile * (kBN * D * 2);
+    const uint32_t g0k = (uint32_t)tile * (kBN * 2u) * k_t;
+    const uint32_t g0v = (uint32_t)tile * (kBN * 2u) * v_t;
     const uint32_t so = (uint32_t)st * kTileBytes;
 #pragma unroll
     for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
       const uint32_t piece = (uint32_t)(wave * T::LOADS_PER_WAVE + i) * 1024u;
-      lds_dma16(rk, lds0 + so + piece, g0 + dk[i]);
-      lds_dma16(rv, lds0 + kVRegion + so + piece, g0 + dv[i]);
+      lds_dma16(rk, lds0 + so + piece, g0k + dk[i]);
+      lds_dma16(rv, lds0 + kVRegion + so + piece, g0v + dv[i]);
     }
   };
 
@@ -582,15 +609,16 @@ void fa_fwd_kernel(FwdParams p) {
     const float inv = 1.0f / l16_tot;
     if (OUT_F32) {
       if (wave_has_rows && qrow < p.Tq) {
-        const size_t orow = ((size_t)cur.bh * (size_t)p.Tq + (size_t)qrow) * D;
+        const int64_t orow = head_off(cur.bh, p.o_b, p.o_h, p.Tq) + (int64_t)qrow * o_t;
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
+            const int col = 32 * db + 8 * i4 + 4 * g;
             const f32x4_t f = {oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv,
                                oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv};
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.o) + orow + 32 * db + 8 * i4 +
-                                        4 * g) = f;
+            if (col < dd)
+              *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.o) + orow + col) = f;
           }
       }
     } else if (wave_has_rows) {
@@ -599,7 +627,8 @@ void fa_fwd_kernel(FwdParams p) {
       // each global store writes whole 128-byte row segments.
       const uint32_t ob = (uint32_t)reinterpret_cast<uintptr_t>(ostage) + (uint32_t)wave * 4096u;
       const int rows = p.Tq - qw0;   // valid rows of this wave (>= 1)
-      uint16_t* const obase = static_cast<uint16_t*>(p.o) + ((size_t)cur.bh * p.Tq + qw0) * D;
+      uint16_t* const obase = static_cast<uint16_t*>(p.o) + head_off(cur.bh, p.o_b, p.o_h, p.Tq) +
+                              (int64_t)qw0 * o_t;
 #pragma unroll
       for (int h = 0; h < ND / 2; ++h) {
 #pragma unroll
@@ -616,8 +645,8 @@ void fa_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int row = 8 * i + (lane >> 3), ch = lane & 7;
           const u32x4_t w = lds_read16u(ob + row * 128u + 16u * (ch ^ (row & 7)));
-          if (row < rows)
-            *reinterpret_cast<u32x4_t*>(obase + (size_t)row * D + 64 * h + 8 * ch) = w;
+          if (row < rows && 64 * h + 8 * ch < dd)
+            *reinterpret_cast<u32x4_t*>(obase + (int64_t)row * o_t + 64 * h + 8 * ch) = w;
         }
       }
     }
@@ -631,7 +660,7 @@ void fa_fwd_kernel(FwdParams p) {
   if (describe(c, 0).pp < PX && !group_b) __syncthreads();   // match group B's extra barrier
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
 hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -647,6 +676,12 @@ hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
   // A zero scale would make every score 0; a tiny positive factor gives the same softmax.
   p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  p.H = a.H;
+  p.d = a.d;
+  p.q_b = a.q_s[0]; p.q_h = a.q_s[1]; p.q_t = (uint32_t)a.q_s[2];
+  p.k_b = a.k_s[0]; p.k_h = a.k_s[1]; p.k_t = (uint32_t)a.k_s[2];
+  p.v_b = a.v_s[0]; p.v_h = a.v_s[1]; p.v_t = (uint32_t)a.v_s[2];
+  p.o_b = a.o_s[0]; p.o_h = a.o_s[1]; p.o_t = (uint32_t)a.o_s[2];
   // One workgroup per CU (each needs a whole CU's LDS), in 8 groups (one per XCD) when there
   // are more block pairs than CUs; otherwise one workgroup per pair.
   int dev = 0, cus = 0;
@@ -664,20 +699,33 @@ hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
     grid = (int)(pairs < cus ? pairs : (cus > 0 ? cus : 1));
   }
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, OUT_F32>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, CAUSAL, OUT_F32, GEN>),
                          dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
+template <int D, bool GEN>
+hipError_t launch_g(const FwdLaunch& a, hipStream_t s) {
+  if (a.causal)
+    return a.out_f32 ? launch<D, true, true, GEN>(a, s) : launch<D, true, false, GEN>(a, s);
+  return a.out_f32 ? launch<D, false, true, GEN>(a, s) : launch<D, false, false, GEN>(a, s);
+}
+
+// the contiguous layout with d = D takes the specialised kernel
 template <int D>
 hipError_t launch_d(const FwdLaunch& a, hipStream_t s) {
-  if (a.causal) return a.out_f32 ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
-  return a.out_f32 ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
+  auto contiguous = [&](const int64_t* st, int T_) {
+    return st[2] == D && st[1] == (int64_t)T_ * D && st[0] == (int64_t)a.H * T_ * D;
+  };
+  const bool plain = a.d == D && contiguous(a.q_s, a.Tq) && contiguous(a.k_s, a.Tk) &&
+                     contiguous(a.v_s, a.Tk) && contiguous(a.o_s, a.Tq);
+  return plain ? launch_g<D, false>(a, s) : launch_g<D, true>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream) {
-  if (a.d == 64) return launch_d<64>(a, stream);
+  // head dimensions up to 64 run the 64-wide kernel, larger ones the 128-wide one, padded
+  if (a.d <= 64) return launch_d<64>(a, stream);
   return launch_d<128>(a, stream);
 }
 

@@ -15,17 +15,30 @@ int map_hip(hipError_t e) {
   return FA_ERR_HIP;
 }
 
-int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-               int64_t h, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale,
+int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+               int64_t h, int64_t Tq, int64_t Tk, int64_t d, const int64_t* qs,
+               const int64_t* ks, const int64_t* vs, const int64_t* os, int causal, float scale,
                void* stream, bool out_f32) {
-  const int st = fa_validate_fwd(q, k, v, o, lse, B, h, Tq, Tk, d, causal, scale);
-  if (st != FA_OK) return st;
   fa::FwdLaunch a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = static_cast<int>(B); a.H = static_cast<int>(h);
   a.Tq = static_cast<int>(Tq); a.Tk = static_cast<int>(Tk); a.d = static_cast<int>(d);
   a.causal = causal != 0; a.out_f32 = out_f32; a.scale = scale;
+  for (int i = 0; i < 3; ++i) {
+    a.q_s[i] = qs[i]; a.k_s[i] = ks[i]; a.v_s[i] = vs[i]; a.o_s[i] = os[i];
+  }
   return map_hip(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+               int64_t h, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale,
+               void* stream, bool out_f32) {
+  const int st = fa_validate_fwd(q, k, v, o, lse, B, h, Tq, Tk, d, causal, scale);
+  if (st != FA_OK) return st;
+  // contiguous [B][h][T][d]
+  const int64_t qs[3] = {h * Tq * d, Tq * d, d}, ks[3] = {h * Tk * d, Tk * d, d};
+  return fwd_launch(q, k, v, o, lse, B, h, Tq, Tk, d, qs, ks, ks, qs, causal, scale, stream,
+                    out_f32);
 }
 }  // namespace
 
@@ -39,6 +52,18 @@ extern "C" int fa_fwd_o32(const void* q, const void* k, const void* v, float* o,
                           int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
                           int causal, float scale, void* stream) {
   return fwd_common(q, k, v, o, lse, B, h, Tq, Tk, d_head, causal, scale, stream, true);
+}
+
+extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                              const int64_t* q_strides, const int64_t* k_strides,
+                              const int64_t* v_strides, const int64_t* o_strides, int causal,
+                              float scale, void* stream) {
+  const int st = fa_validate_fwd_strided(q, k, v, o, lse, B, h, Tq, Tk, d_head, q_strides,
+                                         k_strides, v_strides, o_strides, causal, scale);
+  if (st != FA_OK) return st;
+  return fwd_launch(q, k, v, o, lse, B, h, Tq, Tk, d_head, q_strides, k_strides, v_strides,
+                    o_strides, causal, scale, stream, false);
 }
 
 extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -16,6 +16,8 @@ struct FwdLaunch {
   bool causal;
   bool out_f32;
   float scale;
+  // element strides (batch, head, row) of q, k, v, o; the last dimension is contiguous
+  int64_t q_s[3], k_s[3], v_s[3], o_s[3];
 };
 
 struct DecodeLaunch {

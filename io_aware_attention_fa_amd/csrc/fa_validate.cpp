@@ -12,6 +12,22 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool head_dim_ok(int64_t d) { return d == 64 || d == 128; }
 
+// The forward pads any multiple of 8 up to 128 on chip (16-byte chunks of 8 bf16).
+bool fwd_head_dim_ok(int64_t d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+
+// Strided head: rows of stride t (>= d, a multiple of 8 elements so that rows stay 16-byte
+// aligned), the head's bytes including one 128-row block of reads past the end below 2^31.
+bool strides_ok(const int64_t* s, int64_t T, int64_t d, int64_t B, int64_t h) {
+  if (!s) return false;
+  const int64_t sb = s[0], sh = s[1], st = s[2];
+  if (st < d || st % 8 != 0 || sb < 0 || sh < 0 || sb % 8 != 0 || sh % 8 != 0) return false;
+  if (st > (FA_MAX_HEAD_BYTES / 2) / (T + 128)) return false;
+  // the largest element offset must fit in int64 comfortably
+  const int64_t big = INT64_MAX / 4;
+  if ((B > 1 && sb > big / (B - 1)) || (h > 1 && sh > big / (h - 1))) return false;
+  return true;
+}
+
 // Per-head tensors are addressed with 32-bit byte offsets inside the kernels.
 bool head_bytes_ok(int64_t rows, int64_t d) {
   // one extra 128-row block of zero-filled reads past the end must still fit in 32 bits
@@ -20,12 +36,35 @@ bool head_bytes_ok(int64_t rows, int64_t d) {
 
 }  // namespace
 
+extern "C" int fa_validate_fwd_strided(const void* q, const void* k, const void* v,
+                                       const void* o, const float* lse, int64_t B, int64_t h,
+                                       int64_t Tq, int64_t Tk, int64_t d_head,
+                                       const int64_t* q_strides, const int64_t* k_strides,
+                                       const int64_t* v_strides, const int64_t* o_strides,
+                                       int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!strides_ok(q_strides, Tq, d_head, B, h) || !strides_ok(k_strides, Tk, d_head, B, h) ||
+      !strides_ok(v_strides, Tk, d_head, B, h) || !strides_ok(o_strides, Tq, d_head, B, h))
+    return FA_ERR_SHAPE;
+  const int64_t nqb = (Tq + 127) / 128;
+  if (B > INT32_MAX / h || B * h > INT32_MAX / nqb) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Tq > Tk) return FA_ERR_CAUSAL_TQ_GT_TK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 extern "C" int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
                                int64_t d_head, int causal, float scale) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
-  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!head_bytes_ok(Tq, d_head) || !head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
   // the grid is one workgroup per (128-row query block, head, batch) and must fit in 31 bits
   const int64_t nqb = (Tq + 127) / 128;
@@ -134,7 +173,8 @@ extern "C" const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is < 1 or exceeds the kernels' limits";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d_head must be 64 or 128";
+    case FA_ERR_HEAD_DIM:
+      return "FA_ERR_HEAD_DIM: d_head must be 64 or 128 (forward: a multiple of 8 up to 128)";
     case FA_ERR_CAUSAL_TQ_GT_TK: return "FA_ERR_CAUSAL_TQ_GT_TK: causal attention needs Tq <= Tk";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and causal 0 or 1";

@@ -64,8 +64,13 @@ P = 0x100000   # a 16-byte aligned fake address; validation never dereferences p
     ((P, P, P, P, P, 1, 1, 0, 16, 64, 0, 0.125), 2),
     ((P, P, P, P, P, 1, 1, 16, 0, 64, 0, 0.125), 2),
     ((P, P, P, P, P, 1, 1, 16, 2**30, 128, 0, 0.125), 2),
-    ((P, P, P, P, P, 1, 1, 16, 16, 96, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 16, 16, 100, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 16, 16, 136, 0, 0.125), 3),
     ((P, P, P, P, P, 1, 1, 16, 16, 256, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 16, 16, 4, 0, 0.125), 3),
+    ((P, P, P, P, P, 1, 1, 16, 16, 96, 0, 0.125), 0),
+    ((P, P, P, P, P, 1, 1, 16, 16, 80, 0, 0.125), 0),
+    ((P, P, P, P, P, 1, 1, 16, 16, 8, 0, 0.125), 0),
     ((P, P, P, P, P, 1, 1, 17, 16, 64, 1, 0.125), 4),
     ((P, P, P, P, P, 1, 1, 16, 17, 64, 1, 0.125), 0),
     ((P, P, P, P, P, 1, 1, 17, 16, 64, 0, 0.125), 0),
@@ -112,7 +117,7 @@ def test_invalid_calls_touch_nothing(fa_lib):
     lse = np.full(64, 12345.0, dtype=np.float32)
     ws = np.full(4096, 7, dtype=np.uint8)
     a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, o, lse)]
-    st = _lib.lib.fa_fwd(*a, 1, 1, 16, 16, 96, 0, 0.125, None)
+    st = _lib.lib.fa_fwd(*a, 1, 1, 16, 16, 100, 0, 0.125, None)
     assert st == 3
     st = _lib.lib.fa_fwd_o32(*a, 1, 1, 17, 16, 64, 1, 0.125, None)
     assert st == 4
@@ -207,3 +212,28 @@ def test_validate_gelu(fa_lib, args, code):
 ])
 def test_validate_bias_gelu_dropout(fa_lib, args, code):
     assert fa_lib.fa_validate_bias_gelu_dropout(*args) == code
+
+
+def _vs(fa_lib, **kw):
+    a = dict(B=2, h=3, Tq=100, Tk=120, d=80, causal=1, scale=0.1,
+             qs=(3 * 100 * 80, 100 * 80, 80), ks=(120 * 3 * 80, 80, 3 * 80),
+             vs=(120 * 3 * 80, 80, 3 * 80), os=(3 * 100 * 80, 100 * 80, 80))
+    a.update(kw)
+    return fa_lib.fa_validate_fwd_strided(P, P, P, P, P, a["B"], a["h"], a["Tq"], a["Tk"], a["d"],
+                                          a["qs"], a["ks"], a["vs"], a["os"], a["causal"],
+                                          a["scale"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"d": 128, "qs": (0, 0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 0, 128)}, 0),
+    ({"qs": None}, 2),
+    ({"ks": (120 * 3 * 80, 80, 72)}, 2),            # row stride below d
+    ({"ks": (120 * 3 * 80, 80, 3 * 80 + 4)}, 2),    # row stride not a multiple of 8
+    ({"vs": (120 * 3 * 80, 84, 3 * 80)}, 2),        # head stride not a multiple of 8
+    ({"os": (-8, 100 * 80, 80)}, 2),                # negative stride
+    ({"ks": (0, 0, 2**26)}, 2),                      # head beyond 2^31 bytes
+    ({"d": 100}, 3), ({"Tq": 121}, 4),
+])
+def test_validate_fwd_strided(fa_lib, kw, code):
+    assert _vs(fa_lib, **kw) == code
