@@ -18,6 +18,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
              (one read and one write of the matrix) against the HBM peak
   gelu, bias_gelu_dropout = the fused elementwise chains on the pages' workloads (64M fp32
              values; a 4096 x 8192 bf16 activation with p = 0.1), timed separately: HBM GB/s
+  layouts  = the forward on strided [B][T][h][d] inputs at the prefill shape, and at d_head = 80
+             (20 heads, padded to 128 on chip), timed separately: TFLOP/s of the true d_head
 """
 from __future__ import annotations
 
@@ -235,6 +237,46 @@ def measure_softmax(args, fa, si, torch):
     return res
 
 
+def measure_layouts(args, fa, si, cm, torch):
+    """The forward on layout variants: the prefill workload with q, k, v in [B][T][h][d] (strided
+    views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the pages' padding example."""
+    import numpy as np
+    peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
+    K = args.extra_steps or 20
+    res = {}
+    for key, (B, h, T, d, strided) in {"bthd": (8, 32, 4096, 128, True),
+                                        "d80": (8, 20, 4096, 80, False)}.items():
+        wl = si.custom_workload(B, h, T, T, d, True, name=key)
+        q, k, v = si.make_inputs(wl, seed=0)
+        if strided:
+            def bthd(bits):
+                return upload(np.ascontiguousarray(bits.transpose(0, 2, 1, 3))).transpose(1, 2)
+            tq, tk, tv = bthd(q), bthd(k), bthd(v)
+            call = lambda: fa.fa_fwd_strided(tq, tk, tv, causal=True, scale=wl.scale)
+        else:
+            tq, tk, tv = upload(q), upload(k), upload(v)
+            o = torch.empty_like(tq)
+            lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
+            call = lambda: fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse)
+        del q, k, v
+        ms = time_calls(torch, call, 3, K)
+        flops = cm.attention_flops(B, h, T, T, d, True)
+        tf = flops / (ms * 1e-3) / 1e12
+        eprint(f"[bench] layout {key}: B={B} h={h} T={T} d={d} avg {ms:.4f} ms  {tf:.1f} TFLOP/s  "
+               f"{100 * tf / peak:.1f}% of {peak:.0f}")
+        res[key] = {"metric": f"attention fwd TFLOP/s, causal, d_head={d}" +
+                              (", [B][T][h][d] inputs" if strided else ", padded to 128 on chip"),
+                    "value": tf, "unit": "TFLOP/s", "steps": K, "warmup": 3, "avg_ms": ms,
+                    "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                                 "frac": tf / peak, "traffic": None},
+                    "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
+                               "layout": "BTHD strided" if strided else "BHTD contiguous",
+                               "flops": flops}}
+        del tq, tk, tv
+        torch.cuda.empty_cache()
+    return res
+
+
 def measure_elementwise(args, fa, si, torch):
     """GELU on the pages' 64M fp32 values and bias-GELU-dropout on a 4096 x 8192 bf16
     activation (p = 0.1); each HBM GB/s counts one read and one write of the tensor."""
@@ -308,7 +350,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax", "elementwise"],
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax", "elementwise",
+                                       "layouts"],
                     default=None,
                     help="run one half of the step (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -357,6 +400,7 @@ def main():
     do_backward = args.only == "backward" or (args.only is None and not args.no_backward)
     do_softmax = args.only == "softmax" or (args.only is None and not args.no_extras)
     do_elementwise = args.only == "elementwise" or (args.only is None and not args.no_extras)
+    do_layouts = args.only == "layouts" or (args.only is None and not args.no_extras)
     wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
 
     t0 = time.perf_counter()
@@ -368,6 +412,18 @@ def main():
                "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "roofline": sm["roofline"], "config": {"workload": "softmax_rows_4096x4096_f32"},
                "cpu_baseline": sm.get("cpu_baseline")}
+        print(json.dumps(out), flush=True)
+        return
+
+    if args.only == "layouts":
+        lay = measure_layouts(args, fa, si, cm, torch)
+        b = lay["bthd"]
+        out = {"metric": b["metric"], "value": b["value"], "unit": b["unit"], "n_gpus": 1,
+               "steps": b["steps"], "warmup": b["warmup"], "ms_per_step": b["avg_ms"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic", "roofline": b["roofline"],
+               "config": {"workload": "causal_b8_h32_t4096_d128 in [B][T][h][d]"},
+               "cpu_baseline": None, "layouts": lay}
         print(json.dumps(out), flush=True)
         return
 
@@ -498,6 +554,8 @@ def main():
         out["softmax"] = measure_softmax(args, fa, si, torch)
     if do_elementwise:
         out.update(measure_elementwise(args, fa, si, torch))
+    if do_layouts:
+        out["layouts"] = measure_layouts(args, fa, si, cm, torch)
     print(json.dumps(out), flush=True)
 
 
