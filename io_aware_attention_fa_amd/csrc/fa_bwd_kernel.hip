@@ -11,23 +11,26 @@
 // MI355X mapping (our design, not the pages'): three kernels on the caller's stream.
 //   * fa_bwd_prep: D_i and LSE_i * log2(e) per query row into the workspace (HBM-bound, one
 //     pass over O and dO).
-//   * fa_bwd_dkdv: one workgroup per (128-key block, head); each lane owns one key.  Q, dO and
-//     the per-row L, D stream through LDS in 64-row tiles; K and V stay in registers as MFMA B
-//     operands.  Per tile: S = Q K^T and dP = dO V^T (A operands: Q and dO rows from LDS),
-//     then P and dS in the lane-per-key layout, then dV^T += dO^T P and dK^T += Q^T dS with
-//     dO^T and Q^T read by the transposing LDS read (ds_read_b64_tr_b16) from the same
-//     row-major tiles.  No atomics: every key's dK and dV are finished by one workgroup.
-//   * fa_bwd_dq: one workgroup per (128-query block, head); each lane owns one query.  K and V
-//     stream through LDS; S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
+//   * fa_bwd_dkdv: one workgroup of 8 waves per (128-key block, head); each lane owns one key.
+//     Q, dO and the per-row L, D stream through LDS in 32-row tiles; K and V stay in registers
+//     as MFMA B operands.  The two waves on a SIMD own the same 32 keys and split the work: one
+//     computes S = Q K^T, P, dS and dK^T += Q^T dS, the other dP = dO V^T and dV^T += dO^T P;
+//     they exchange P and dP - D through LDS.  dO^T and Q^T come from the transposing LDS read
+//     (ds_read_b64_tr_b16) of the same row-major tiles.  No atomics: every key's dK and dV are
+//     finished by one workgroup.
+//   * fa_bwd_dq: one workgroup of 8 waves per (256-query block, head); each lane owns one query.
+//     K and V stream through LDS; S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
 //     dQ^T += K^T dS^T with K^T from the transposing read.  The two gradient kernels share no
 //     partial sums, so the result is deterministic.
 //   * A tile's 16-byte chunks are XOR-swizzled by row so that both the row reads (16 rows x one
 //     chunk per 16 lanes) and the transposing reads (4 rows x 4 chunks per 32 lanes) hit
 //     distinct LDS banks; tiles are filled by direct global-to-LDS loads into a ring of stages,
 //     several tiles ahead.
-//   * Each gradient kernel is a software pipeline with one wave per SIMD (see below): the
-//     exp / dS work of one tile is scheduled between the MFMAs of the gradient products of the
-//     tile before, and every MFMA operand streams from LDS through a register ring.
+//   * Both gradient kernels run two waves per SIMD (each wave's state fits in half of the SIMD's
+//     registers), so one wave's LDS reads and vector work overlap the other's MFMAs; within a
+//     wave, software pipelining schedules the exp / dS work of one tile between the MFMAs of the
+//     gradient products of the tile before, and every MFMA operand streams from LDS through a
+//     register ring.
 //   * Ragged tails: buffer loads return zeros past the end of a head, so out-of-range rows
 //     contribute nothing; out-of-range keys and causally hidden entries get P = 0.
 //   * MFMA v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (round to nearest
@@ -44,10 +47,12 @@
 namespace fa {
 namespace {
 
-constexpr int kOwn = 128;     // own rows (keys or queries) per workgroup
-constexpr int kWaves = 4;     // one wave per SIMD, 32 own rows each
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 8;      // MFMA operands in flight
+constexpr int kOwnK = 128;    // dK/dV: keys per workgroup
+constexpr int kWavesK = 8;    // dK/dV: four wave pairs, two waves per SIMD
+constexpr int kThreadsK = 64 * kWavesK;
+constexpr int kWavesQ = 8;    // dQ: two waves per SIMD, 32 own queries each
+constexpr int kOwnQ = 32 * kWavesQ;
+constexpr int kThreadsQ = 64 * kWavesQ;
 
 struct BwdParams {
   const uint16_t* q;
@@ -59,22 +64,22 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  int Tq, Tk, BH, nblk;   // nblk: 128-row own blocks per head
+  int Tq, Tk, BH, nblk;   // nblk: own blocks (128 keys or 256 queries) per head
   int groups;             // 8: workgroup n works on heads n % 8, n % 8 + 8, ... (XCD-local)
   float c;                // scale * log2(e)
   float scale;
 };
 
-// A streamed tile of ROWS rows of D bf16 and how the 4 waves load it.
-template <int D, int ROWS>
+// A streamed tile of ROWS rows of D bf16 and how the W waves of a workgroup load it.
+template <int D, int ROWS, int W>
 struct BTile {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int TILE = ROWS * D;              // bf16 per tile
   static constexpr uint32_t BYTES = TILE * 2;
   static constexpr int ROWS_PER_LOAD = 64 / CH;      // rows one 64-lane 1 KB load covers
   static constexpr int LOADS = ROWS / ROWS_PER_LOAD;
-  static constexpr int LPW = LOADS / kWaves;         // 1 KB loads per wave per tile
-  static_assert(LPW >= 1 && LOADS % kWaves == 0, "staging layout");
+  static constexpr int LPW = LOADS / W;              // 1 KB loads per wave per tile
+  static_assert(LPW >= 1 && LOADS % W == 0, "staging layout");
   // Row term of the chunk swizzle (physical chunk = logical chunk ^ f(r), an involution).
   // d = 128: a row is 256 bytes (all 64 banks); f takes 16 distinct values over rows 0..15
   // (row reads) and moves each of 4 consecutive rows to its own 64-byte quarter (transposing
@@ -92,9 +97,9 @@ struct BTile {
 //  32*db + 16*dh + 4*(l % 4), and receives tile^T row 32*db + (l % 32) at rows
 //  16*ks + 8*hf + 4*g + 0..3.  The swizzle depends on the row through (l % 16) / 4, g and hf
 //  only, which makes this (tr_off ^ (64*db) ^ (32*hf)) + (16*ks + 8*hf) rows.
-template <int D, int ROWS>
+template <int D, int ROWS, int W>
 struct Lanes {
-  using T = BTile<D, ROWS>;
+  using T = BTile<D, ROWS, W>;
   uint32_t row_off, tr_off;
   uint32_t dma_l[T::LPW], dma_g[T::LPW];   // LDS / global byte offsets of this wave's loads
   __device__ __forceinline__ Lanes(int wave, int lane) {
@@ -125,12 +130,19 @@ struct Region {
   uint32_t row[D / 16], tr[D / 32][2];
   __device__ __forceinline__ Region(uint32_t base, uint32_t row_off, uint32_t tr_off) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) row[s] = base + (row_off ^ (32u * (uint32_t)s));
+    for (int s = 0; s < D / 16; ++s) {
+      row[s] = base + (row_off ^ (32u * (uint32_t)s));
+      // opaque to the optimiser: a base above 64 KB would otherwise be folded into per-stage
+      // addresses (beyond the 16-bit LDS immediate) that are kept in registers
+      asm volatile("" : "+v"(row[s]));
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < 2; ++hf) {
         tr[db][hf] = base + (tr_off ^ (64u * (uint32_t)db) ^ (32u * (uint32_t)hf));
+        asm volatile("" : "+v"(tr[db][hf]));
+      }
   }
   // A operand: rows 32*blk + (lane % 32), k-step s, of the tile at byte offset so
   __device__ __forceinline__ bf16x8_t row_opnd(uint32_t so, int blk, int s) const {
@@ -210,32 +222,34 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 //   A: the score-side products (S and dP) of the tile, from row operands in LDS;
 //   V: the elementwise part, P = exp2(S * scale * log2 e - L2), dS = P (dP - D), rounded to bf16;
 //   C: the gradient products that consume P and dS, from transposed operands in LDS.
-// Step s runs C of tile s - 1 with V of tile s scheduled between its MFMAs (one wave per SIMD:
-// the vector instructions issue while the matrix core works), then A of tile s + 1; V of tile s
+// Step s runs C of tile s - 1 with V of tile s scheduled between its MFMAs (the vector
+// instructions issue while the matrix core works), then A of tile s + 1; V of tile s
 // reads the score registers that A filled in the step before.  The bf16 P / dS operands are
-// double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring of kRing
-// registers, each read issued kRing MFMAs ahead of its use, and the ring runs across steps: the
-// last MFMAs of step s read the first operands of step s + 1 (C operands of tile s, resident),
-// before the barrier that ends the step.  Tiles are loaded AHEAD steps ahead into a ring of NST
+// double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring of
+// registers, each read issued as many MFMAs ahead of its use as the ring holds, and the ring
+// runs across steps: the last MFMAs of step s read the first operands of step s + 1 (C operands
+// of tile s, resident), before the barrier that ends the step.  Tiles are loaded AHEAD steps ahead into a ring of NST
 // stages; the stage of every step is a compile-time constant (the steady-state loop dispatches
 // on s % NST), so that all LDS addresses are per-lane registers plus immediates.  The last two
 // steps run all three parts: their V and A parts read stages holding stale tiles and produce
 // values that are never used.
 
 // A step's MFMA stream: NC C-part MFMAs (two transposing reads each), then NA A-part MFMAs (one
-// read each).  PRE: the ring arrived preloaded; NEXT: the last kRing MFMAs read the next step's
-// first operands (C operands, two reads each).  VPM vector instructions are scheduled after each
-// C-part MFMA (after each A-part MFMA when the step has no C part), and XR extra LDS reads are
-// issued up front.
-template <int NC, int NA, int VPM, int XR, bool PRE, bool NEXT>
+// read each), or the A part first if AFIRST.  PRE: the ring arrived preloaded; NEXT: the last
+// RING MFMAs read the next step's first operands (C operands, two reads each).  VPM vector
+// instructions are scheduled after each C-part MFMA (after each A-part MFMA when the step has
+// no C part), XR extra LDS reads are issued up front, and RING operands are in flight.
+template <int NC, int NA, int VPM, int XR, bool PRE, bool NEXT, int RING, bool AFIRST = false>
 struct StepSeq {
   static constexpr int n = NC + NA;
+  static constexpr int kRing = RING;
   static_assert(n % kRing == 0, "the ring restarts at slot 0 every step");
-  static constexpr __device__ int reads(int i) { return i < NC ? 2 : 1; }
+  static constexpr __device__ bool is_c(int i) { return AFIRST ? i >= NA : i < NC; }
+  static constexpr __device__ int reads(int i) { return is_c(i) ? 2 : 1; }
   static constexpr __device__ int refill_reads(int i) {
     return i + kRing < n ? reads(i + kRing) : (NEXT ? 2 : 0);
   }
-  static constexpr __device__ int valu(int i) { return (NC > 0 ? i < NC : i < NA) ? VPM : 0; }
+  static constexpr __device__ int valu(int i) { return (NC > 0 ? is_c(i) : true) ? VPM : 0; }
   static constexpr __device__ int initial_reads() {
     int r = XR;
     if (!PRE)
@@ -292,21 +306,40 @@ __device__ __forceinline__ void wait_tile(int need, int last) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (128-key block, head), lane = key; query tiles of 32 rows.
+// dK, dV: one workgroup of 8 waves per (128-key block, head), lane = key; query tiles of 32 rows.
+// Waves w and w + 4 (which share a SIMD) own the same 32 keys and split the work: wave w (role K)
+// holds the K rows and computes S, P, dS and dK; wave w + 4 (role V) holds the V rows and
+// computes dP - D and dV.  They exchange P (bf16, the operand of dV) and dP - D (fp32) through
+// LDS, double-buffered by tile parity.  Each role holds half of a key block's state, so two
+// waves fit per SIMD and one's LDS reads and vector work overlap the other's MFMAs.
+//   role K, step s: dK += Q^T dS of tile s - 1, with P and dS of tile s (from S, computed in the
+//     step before, and dP - D of tile s from role V) scheduled between its MFMAs; then S of
+//     tile s + 1.  P of tile s goes to LDS.
+//   role V, step s: dP - D of tile s + 1 (the accumulator starts from -D), then dV += dO^T P of
+//     tile s - 1 (P from LDS); dP - D of tile s + 1 goes to LDS.
+// Both roles end every step at the same barrier, which publishes the exchanged tiles.
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int R = 32;        // query rows per streamed tile (one 32-row MFMA block)
-  constexpr int NST = 8;       // LDS stages
+  constexpr int NST = 6;       // LDS stages
   constexpr int AHEAD = 4;     // step s requests tile s + AHEAD
-  using T = BTile<D, R>;
+  constexpr int kRing = 4;     // MFMA operands in flight
   constexpr int NS = D / 16;   // k-steps over d
   constexpr int ND = D / 32;   // 32-row blocks of dK^T / dV^T
-  constexpr int NA = 2 * NS;   // S and dP MFMAs per tile
-  constexpr int NC = 4 * ND;   // dV^T and dK^T MFMAs per tile (two 16-query k-steps)
+  constexpr int NA = NS;       // S (or dP) MFMAs per tile
+  constexpr int NC = 2 * ND;   // dK^T (or dV^T) MFMAs per tile (two 16-query k-steps)
+  // Staging: every wave issues the same number of 1 KB loads per tile.  d = 128: each wave loads
+  // one piece of Q and one of dO; d = 64 (four pieces per tile): waves 0-3 load Q, 4-7 load dO.
+  constexpr bool SPLIT = BTile<D, R, 4>::LOADS < kWavesK;
+  using T = BTile<D, R, SPLIT ? 4 : kWavesK>;
   constexpr int LDS_LD = 64;   // floats of L2 (and of -D) per stage (one 64-lane load)
-  // LDS: Q stages, dO stages, then L2 and -D per stage.
+  constexpr uint32_t XB = 16u * 64u * 4u;   // dP - D of one tile and wave pair: 4 x 64 x 16 B
+  constexpr uint32_t PB = 16u * 64u * 2u;   // P of one tile and wave pair (bf16): 2 x 64 x 16 B
+  // LDS: Q stages, dO stages, L2 and -D per stage, then the exchange buffers [pair][parity].
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float lds_x[4 * 2 * XB / 4];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_p[4 * 2 * PB / 2];
   __shared__ __attribute__((aligned(256))) float lds_ld[2 * NST * LDS_LD];
   const uint32_t lq = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t ldo = lq + NST * T::BYTES;
@@ -315,36 +348,23 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wave & 3;     // wave pair
   const int g = lane >> 5;
-  const Lanes<D, R> ln(wave, lane);
+  const Lanes<D, R, SPLIT ? 4 : kWavesK> ln(SPLIT ? pr : wave, lane);
+  // this lane's slots of the pair's exchange buffers (parity and part add immediates)
+  const uint32_t xb =
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_x) + (uint32_t)pr * (2 * XB) + 16u * lane;
+  const uint32_t pbb =
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_p) + (uint32_t)pr * (2 * PB) + 16u * lane;
 
   int bh, blk;
   block_of(p, false, bh, blk);
   const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
-  const int kw0 = blk * kOwn + wave * 32;   // this wave's first key
-  const int key = kw0 + (lane & 31);
-  // P is zeroed for queries below thr: keys past the end see nothing; causal keys see queries
-  // from key - off on
-  const int thr = key >= p.Tk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
-
-  // K and V rows of this lane's key as B operands (k = 8 columns per lane half).
-  bf16x8_t kf[NS], vf[NS];
-  {
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(p.k + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(p.v + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint32_t o = (uint32_t)(key * D + 16 * s + 8 * g) * 2u;
-      kf[s] = as_bf16x8(buf_load16(rk, o));
-      vf[s] = as_bf16x8(buf_load16(rv, o));
-    }
-  }
+  const int key = blk * kOwnK + pr * 32 + (lane & 31);
 
   // query tiles this block needs: from the first query that sees its first key
   const int nqt = (p.Tq + R - 1) / R;
-  const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwn - off) / R) : 0;
+  const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwnK - off) / R) : 0;
   const int nt = nqt - t0;
 
   const u32x4_t rq = rsrc_words(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
@@ -353,12 +373,17 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const u32x4_t rl = rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
   const u32x4_t rd = rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
   auto request = [&](int it) {   // tile t0 + it into stage it % NST
-    const int st = it & (NST - 1);
+    const int st = it % NST;
     const uint32_t g0 = (uint32_t)(t0 + it) * (R * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
-      lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
-      lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+      if (SPLIT) {
+        const bool qw = wave < 4;
+        lds_dma16(qw ? rq : rdo, (qw ? lq : ldo) + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+      } else {
+        lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+        lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+      }
     }
     // every wave writes the same 64 values of L2 and -D from the tile's first row on
     // (identical data, so the copies agree; the tile uses the first 32)
@@ -366,70 +391,139 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     lds_dma4(rl, ll + st * (LDS_LD * 4), r0);
     lds_dma4(rd, ld + st * (LDS_LD * 4), r0);
   };
-  constexpr int PER = 2 * T::LPW + 2;   // vector-memory operations per tile and wave
+  constexpr int PER = (SPLIT ? 1 : 2) * T::LPW + 2;   // vector-memory operations per tile
 
-  f32x16_t accv[ND], acck[ND];
+  // K (role K) or V (role V) rows of this lane's key as B operands (k = 8 columns per half).
+  bf16x8_t kvf[NS];
+  {
+    const uint16_t* src = wave < 4 ? p.k : p.v;
+    const __amdgpu_buffer_rsrc_t rkv =
+        make_rsrc(src + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    accv[db] = f32x16_t{};
-    acck[db] = f32x16_t{};
+    for (int s = 0; s < NS; ++s)
+      kvf[s] = as_bf16x8(buf_load16(rkv, (uint32_t)(key * D + 16 * s + 8 * g) * 2u));
   }
-  f32x16_t sacc, dpacc;           // S then P, dP - D then dS (32 queries x this key)
-  bf16x8_t pb[2][2], dsb[2][2];   // [tile parity][k-step]: P and dS as C operands
-  bf16x8_t ring[kRing];
-  const Region<D> rQ(lq, ln.row_off, ln.tr_off), rO(ldo, ln.row_off, ln.tr_off);
 
-  // Step s with stage ST = s % NST.  In the MFMA result layout, register i holds query
-  // R*(t0 + s) + 8*(i/4) + 4*g + i%4 for key `key`.
-  auto step = [&](auto parts, auto stage, const int s) {
-    using PT = decltype(parts);
-    constexpr int ST = decltype(stage)::value;
-    constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-    constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-    using S = StepSeq<nc, na, PT::v ? 6 : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next>;
-    constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
-    constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
-    constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
-    constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // operand parities
-    if (s + AHEAD < nt) request(s + AHEAD);
-    // C operand i of the tile at byte offset so: k-step i / (2 ND), column block, Q or dO
-    auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t {
-      const int r = i % (2 * ND);
-      return ((r & 1) ? rQ : rO).tr_opnd(so, r >> 1, i / (2 * ND));
-    };
-    auto opnd = [&](int i) -> bf16x8_t {
-      if (i < nc) return c_opnd(so_c, i);
-      const int j = i - nc;
-      return ((j & 1) ? rO : rQ).row_opnd(so_a, 0, j >> 1);
-    };
-    if constexpr (!PT::c) {
+  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
+  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and the K/V rows)
+  __syncthreads();
+
+  f32x16_t acc[ND];   // dK^T (role K) or dV^T (role V)
 #pragma unroll
-      for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
-    }
-    if constexpr (PT::v) {
-      // dpacc holds dP - D (its A part started from -D)
-      f32x4_t L4[4];
+  for (int db = 0; db < ND; ++db) acc[db] = f32x16_t{};
+  bf16x8_t ring[kRing];
+
+  if (wave < 4) {
+    // ------------------------------- role K -------------------------------
+    // P is zeroed for queries below thr: keys past the end see nothing; causal keys see
+    // queries from key - off on.  thr4: thr relative to the first query this lane holds.
+    const int thr4 = key >= p.Tk ? (1 << 30) : (CAUSAL ? key - off - 4 * g : -(1 << 30));
+    f32x16_t sacc;                // S of the next tile (32 queries x this key)
+    bf16x8_t dsb[2][2];           // [tile parity][k-step]: dS as C-part operands
+    const Region<D> rQ(lq, ln.row_off, ln.tr_off);
+    // vector instructions per C-part MFMA: about 6 per score, 16 scores per lane
+    constexpr int VPM = 12;
+    auto step = [&](auto parts, auto stage, int s) {
+      using PT = decltype(parts);
+      constexpr int ST = decltype(stage)::value;
+      constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+      constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+      using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 8 : 0, PT::c, next, kRing>;
+      constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+      constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
+      constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
+      constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // parities (NST is even)
+      asm volatile("" : "+s"(s));
+      if (s + AHEAD < nt) request(s + AHEAD);
+      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rQ.tr_opnd(so, i % ND, i / ND); };
+      auto opnd = [&](int i) -> bf16x8_t {
+        if (i < nc) return c_opnd(so_c, i);
+        return rQ.row_opnd(so_a, 0, i - nc);
+      };
+      if constexpr (!PT::c) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
-      const int q0 = (t0 + s) * R + 4 * g;
+        for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+      }
+      if constexpr (PT::v) {
+        f32x4_t L4[4], X4[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int a = i >> 2, e = i & 3;
-        float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
-        if (q0 + 8 * a + e < thr) pv = 0.f;
-        sacc[i] = pv;
-        dpacc[i] = pv * dpacc[i];
+        for (int a = 0; a < 4; ++a) {
+          L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
+          X4[a] = lds_read_f32x4(xb + PV * XB + 1024u * a);
+        }
+        const int lt = thr4 - (t0 + s) * R;
+        f32x16_t ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int a = i >> 2, e = i & 3;
+          float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
+          if (8 * a + e < lt) pv = 0.f;
+          sacc[i] = pv;
+          ds[i] = pv * X4[a][e];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          lds_write_bf16x8(pbb + PV * PB + 1024u * ks, pack_kstep(sacc, ks));
+          dsb[PV][ks] = pack_kstep(ds, ks);
+        }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pb[PV][ks] = pack_kstep(sacc, ks);
-        dsb[PV][ks] = pack_kstep(dpacc, ks);
+      for (int i = 0; i < S::n; ++i) {
+        const bf16x8_t a = ring[i % kRing];
+        if (i + kRing < S::n)
+          ring[i % kRing] = opnd(i + kRing);
+        else if (next)
+          ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
+        if (i < nc) {
+          acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
+        } else {
+          const int j = i - nc;
+          sacc = mfma_32x32x16(a, kvf[j], j == 0 ? f32x16_t{} : sacc);
+        }
+      }
+      sched_pattern<S>();
+      // the next step's A part reads tile s + 2
+      wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
+      __syncthreads();
+    };
+    // steps -1 .. nt (see the pipeline above)
+    step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
+    step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+    {
+      using P = Parts<true, true, true, true>;
+      int s = 1;
+      for (;;) {
+        step(P{}, Stage<1>{}, s); if (++s > nt) break;
+        step(P{}, Stage<2>{}, s); if (++s > nt) break;
+        step(P{}, Stage<3>{}, s); if (++s > nt) break;
+        step(P{}, Stage<4>{}, s); if (++s > nt) break;
+        step(P{}, Stage<5>{}, s); if (++s > nt) break;
+        step(P{}, Stage<0>{}, s); if (++s > nt) break;
       }
     }
-    // the next tile's dP accumulator starts from -D of its rows
-    f32x16_t nd0;
-    if constexpr (PT::a) {
+  } else {
+    // ------------------------------- role V -------------------------------
+    const Region<D> rO(ldo, ln.row_off, ln.tr_off);
+    f32x16_t dpacc;   // dP - D of the next tile
+    auto step = [&](auto parts, auto stage, int s) {
+      using PT = decltype(parts);
+      constexpr int ST = decltype(stage)::value;
+      constexpr int nc = PT::c ? NC : 0;
+      using S = StepSeq<nc, NA, 0, PT::c ? 6 : 4, false, false, kRing, true>;
+      constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+      constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
+      constexpr int PX = (ST + 1) & 1;   // parity of tiles s - 1 and s + 1
+      asm volatile("" : "+s"(s));
+      if (s + AHEAD < nt) request(s + AHEAD);
+      auto opnd = [&](int i) -> bf16x8_t {
+        if (i < NA) return rO.row_opnd(so_a, 0, i);
+        const int k = i - NA;
+        return rO.tr_opnd(so_c, k % ND, k / ND);
+      };
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) ring[i] = opnd(i);
+      // the dP accumulator starts from -D of the tile's rows
+      f32x16_t nd0;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4_t v4 = lds_read_f32x4(ld + ((ST + 1) % NST) * (LDS_LD * 4) +
@@ -437,85 +531,81 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
       }
-    }
+      bf16x8_t pv[2];   // P of tile s - 1 from role K
+      if constexpr (PT::c) {
 #pragma unroll
-    for (int i = 0; i < S::n; ++i) {
-      const bf16x8_t a = ring[i % kRing];
-      if (i + kRing < S::n)
-        ring[i % kRing] = opnd(i + kRing);
-      else if (next)
-        ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
-      if (i < nc) {
-        const int r = i % (2 * ND), ks = i / (2 * ND);
-        if (r & 1)
-          acck[r >> 1] = mfma_32x32x16(a, dsb[PC][ks], acck[r >> 1]);
-        else
-          accv[r >> 1] = mfma_32x32x16(a, pb[PC][ks], accv[r >> 1]);
-      } else {
-        const int j = i - nc, ss = j >> 1;
-        if (j & 1)
-          dpacc = mfma_32x32x16(a, vf[ss], ss == 0 ? nd0 : dpacc);
-        else
-          sacc = mfma_32x32x16(a, kf[ss], ss == 0 ? f32x16_t{} : sacc);
+        for (int ks = 0; ks < 2; ++ks) pv[ks] = lds_read_bf16x8(pbb + PX * PB + 1024u * ks);
       }
-    }
-    sched_pattern<S>();
-    // the next step's A part reads tile s + 2
-    wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
-    __syncthreads();
-  };
-
-  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
-  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and K, V rows)
-  __syncthreads();
-  // steps -1 .. nt (see the pipeline above)
-  step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
-  step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
-  // steps 1 .. nt: a chain of the NST stage variants, left after step nt
-  {
-    using P = Parts<true, true, true, true>;
-    int s = 1;
-    for (;;) {
-      step(P{}, Stage<1>{}, s); if (++s > nt) break;
-      step(P{}, Stage<2>{}, s); if (++s > nt) break;
-      step(P{}, Stage<3>{}, s); if (++s > nt) break;
-      step(P{}, Stage<4>{}, s); if (++s > nt) break;
-      step(P{}, Stage<5>{}, s); if (++s > nt) break;
-      step(P{}, Stage<6>{}, s); if (++s > nt) break;
-      step(P{}, Stage<7>{}, s); if (++s > nt) break;
-      step(P{}, Stage<0>{}, s); if (++s > nt) break;
+#pragma unroll
+      for (int i = 0; i < S::n; ++i) {
+        const bf16x8_t a = ring[i % kRing];
+        if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
+        if (i < NA) {
+          dpacc = mfma_32x32x16(a, kvf[i], i == 0 ? nd0 : dpacc);
+        } else {
+          const int k = i - NA;
+          acc[k % ND] = mfma_32x32x16(a, pv[k / ND], acc[k % ND]);
+        }
+      }
+      sched_pattern<S>();
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        lds_write_f32x4(xb + PX * XB + 1024u * a,
+                        f32x4_t{dpacc[4 * a], dpacc[4 * a + 1], dpacc[4 * a + 2], dpacc[4 * a + 3]});
+      wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
+      __syncthreads();
+    };
+    step(Parts<false, false, true, false>{}, Stage<NST - 1>{}, -1);
+    step(Parts<false, false, true, false>{}, Stage<0>{}, 0);
+    {
+      using P = Parts<true, false, true, false>;
+      int s = 1;
+      for (;;) {
+        step(P{}, Stage<1>{}, s); if (++s > nt) break;
+        step(P{}, Stage<2>{}, s); if (++s > nt) break;
+        step(P{}, Stage<3>{}, s); if (++s > nt) break;
+        step(P{}, Stage<4>{}, s); if (++s > nt) break;
+        step(P{}, Stage<5>{}, s); if (++s > nt) break;
+        step(P{}, Stage<0>{}, s); if (++s > nt) break;
+      }
     }
   }
 
   // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
   if (key < p.Tk) {
     const size_t row = ((size_t)bh * (size_t)p.Tk + (size_t)key) * D;
+    void* dst = wave < 4 ? p.dk : p.dv;
+    const float sc = wave < 4 ? p.scale : 1.f;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const size_t e = row + 32 * db + 8 * a + 4 * g;
-        store4<OUT_F32>(p.dv, e, accv[db][4 * a], accv[db][4 * a + 1], accv[db][4 * a + 2],
-                        accv[db][4 * a + 3]);
-        store4<OUT_F32>(p.dk, e, p.scale * acck[db][4 * a], p.scale * acck[db][4 * a + 1],
-                        p.scale * acck[db][4 * a + 2], p.scale * acck[db][4 * a + 3]);
-      }
+      for (int a = 0; a < 4; ++a)
+        store4<OUT_F32>(dst, row + 32 * db + 8 * a + 4 * g, sc * acc[db][4 * a],
+                        sc * acc[db][4 * a + 1], sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup per (128-query block, head), lane = query; key tiles of 64 rows.
+// dQ: one workgroup of 8 waves (two per SIMD) per (256-query block, head); lane = query; key
+// tiles of 32 rows (d = 128) or 64 rows (d = 64).  The per-wave state fits in half of a SIMD's
+// registers, so the two waves of a SIMD overlap one's LDS reads and vector work with the
+// other's MFMAs.
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsQ) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int R = 64;        // keys per streamed tile (two 32-row MFMA blocks)
-  constexpr int NST = 4;       // LDS stages
-  constexpr int AHEAD = 2;     // step s requests tile s + AHEAD
-  using T = BTile<D, R>;
+  constexpr int R = D == 128 ? 32 : 64;   // keys per streamed tile
+  constexpr int KB = R / 32;              // 32-key MFMA blocks per tile
+  constexpr int NK = R / 16;              // 16-key k-steps of the dQ product per tile
+  constexpr int NST = 8;                  // LDS stages
+  constexpr int AHEAD = 4;                // step s requests tile s + AHEAD
+  constexpr int kRing = 4;                // MFMA operands in flight
+  using T = BTile<D, R, kWavesQ>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int NA = 4 * NS;   // S^T and dP^T MFMAs per tile
-  constexpr int NC = 4 * ND;   // dQ^T MFMAs per tile (four 16-key k-steps)
+  constexpr int NA = 2 * KB * NS;   // S^T and dP^T MFMAs per tile
+  constexpr int NC = ND * NK;       // dQ^T MFMAs per tile
+  // vector instructions per C-part MFMA: about 6.5 per score, 16 * KB scores per lane
+  constexpr int VPM = (KB * 16 * 13 / 2 + NC - 1) / NC;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t lv = lk + NST * T::BYTES;
@@ -523,16 +613,18 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
-  const Lanes<D, R> ln(wave, lane);
+  const Lanes<D, R, kWavesQ> ln(wave, lane);
 
   int bh, blk;
   block_of(p, CAUSAL, bh, blk);   // causal: the longest key ranges (last query blocks) first
   const int off = p.Tk - p.Tq;
-  const int i0 = blk * kOwn;
+  const int i0 = blk * kOwnQ;
   const int qw0 = i0 + wave * 32;
   const int qrow = qw0 + (lane & 31);
-  // keys above lim get P = 0 (past the end, or above the diagonal)
+  // keys above lim get P = 0 (past the end, or above the diagonal); lim4 is lim relative to the
+  // first key this lane holds in a tile
   const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+  const int lim4 = lim - 4 * g;
 
   // Q and dO rows of this lane's query as B operands, and its L2 and -D.
   bf16x8_t qf[NS], dof[NS];
@@ -555,7 +647,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
   }
 
   int kend = p.Tk;
-  if (CAUSAL) kend = min(p.Tk, min(i0 + kOwn, p.Tq) + off);
+  if (CAUSAL) kend = min(p.Tk, min(i0 + kOwnQ, p.Tq) + off);
   const int nt = __builtin_amdgcn_readfirstlane((kend + R - 1) / R);
 
   const u32x4_t rk = rsrc_words(p.k + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
@@ -574,19 +666,22 @@ void fa_bwd_dq_kernel(BwdParams p) {
   f32x16_t accq[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) accq[db] = f32x16_t{};
-  f32x16_t sacc[2], dpacc[2];   // [32-key block]: S^T, dP^T (then dS^T)
-  bf16x8_t dsb[2][4];           // [tile parity][k-step]: dS^T as C operands
+  f32x16_t sacc[KB], dpacc[KB];   // [32-key block]: S^T, dP^T (then dS^T)
+  bf16x8_t dsb[2][NK];            // [tile parity][k-step]: dS^T as C operands
   bf16x8_t ring[kRing];
   const Region<D> rK(lk, ln.row_off, ln.tr_off), rV(lv, ln.row_off, ln.tr_off);
 
   // Step s with stage ST = s % NST.  Register i of 32-key block kb holds key
-  // 64*s + 32*kb + 8*(i/4) + 4*g + i%4 for query `qrow`.
-  auto step = [&](auto parts, auto stage, const int s) {
+  // R*s + 32*kb + 8*(i/4) + 4*g + i%4 for query `qrow`.
+  auto step = [&](auto parts, auto stage, int s) {
     using PT = decltype(parts);
     constexpr int ST = decltype(stage)::value;
     constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
     constexpr bool next = PT::v;
-    using S = StepSeq<nc, na, PT::v ? (PT::m ? 13 : 9) : 0, 0, PT::c, next>;
+    using S = StepSeq<nc, na, PT::v ? VPM : 0, 0, PT::c, next, kRing>;
+    // s as an opaque scalar: otherwise the optimiser keeps a per-lane copy of each value derived
+    // from it for every stage variant of the chain
+    asm volatile("" : "+s"(s));
     constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;
     constexpr uint32_t so_v = ST * T::BYTES;
     constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;
@@ -596,24 +691,24 @@ void fa_bwd_dq_kernel(BwdParams p) {
     auto opnd = [&](int i) -> bf16x8_t {
       if (i < nc) return c_opnd(so_c, i);
       const int j = i - nc;
-      return ((j & 1) ? rV : rK).row_opnd(so_a, (j >> 1) & 1, j >> 2);
+      return ((j & 1) ? rV : rK).row_opnd(so_a, (j >> 1) % KB, (j >> 1) / KB);
     };
     if constexpr (!PT::c) {
 #pragma unroll
       for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
     }
     if constexpr (PT::v) {
-      const int kj0 = s * R + 4 * g;
+      const int lt = lim4 - s * R;   // lim relative to the tile's first key
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
-          if (PT::m && kj0 + 32 * kb + 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
+          if (32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
           dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
         }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+      for (int ks = 0; ks < NK; ++ks) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
     }
 #pragma unroll
     for (int i = 0; i < S::n; ++i) {
@@ -625,7 +720,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
       if (i < nc) {
         accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
       } else {
-        const int j = i - nc, ss = j >> 2, kb = (j >> 1) & 1;
+        const int j = i - nc, ss = (j >> 1) / KB, kb = (j >> 1) % KB;
         if (j & 1)
           dpacc[kb] = mfma_32x32x16(a, dof[ss], ss == 0 ? f32x16_t{} : dpacc[kb]);
         else
@@ -650,6 +745,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
       step(P{}, Stage<1>{}, s); if (++s > nt) break;
       step(P{}, Stage<2>{}, s); if (++s > nt) break;
       step(P{}, Stage<3>{}, s); if (++s > nt) break;
+      step(P{}, Stage<4>{}, s); if (++s > nt) break;
+      step(P{}, Stage<5>{}, s); if (++s > nt) break;
+      step(P{}, Stage<6>{}, s); if (++s > nt) break;
+      step(P{}, Stage<7>{}, s); if (++s > nt) break;
       step(P{}, Stage<0>{}, s); if (++s > nt) break;
     }
   }
@@ -695,19 +794,19 @@ hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
   p.scale = a.scale;
   p.groups = (p.BH % 8 == 0) ? 8 : 1;
   {
-    p.nblk = (a.Tk + kOwn - 1) / kOwn;
+    p.nblk = (a.Tk + kOwnK - 1) / kOwnK;
     void* args[] = {&p};
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32>),
-                        dim3(p.BH * p.nblk), dim3(kThreads), args, 0, stream);
+                        dim3(p.BH * p.nblk), dim3(kThreadsK), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
-    p.nblk = (a.Tq + kOwn - 1) / kOwn;
+    p.nblk = (a.Tq + kOwnQ - 1) / kOwnQ;
     void* args[] = {&p};
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, OUT_F32>),
-                        dim3(p.BH * p.nblk), dim3(kThreads), args, 0, stream);
+                        dim3(p.BH * p.nblk), dim3(kThreadsQ), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -1,5 +1,6 @@
 // LDS staging helpers for gfx950 kernels that stream row-major tiles through shared memory:
-// direct global-to-LDS loads, vector-memory waits, and the LDS reads that feed MFMA operands.
+// direct global-to-LDS loads, vector-memory waits, the LDS reads that feed MFMA operands, and
+// 16-byte LDS writes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,6 +52,16 @@ __device__ __forceinline__ bf16x8_t lds_read_bf16x8(uint32_t addr) {
 __device__ __forceinline__ f32x4_t lds_read_f32x4(uint32_t addr) {
   typedef __attribute__((address_space(3))) const f32x4_t* lds_ptr_t;
   return *(lds_ptr_t)(uintptr_t)addr;
+}
+
+// 16-byte LDS writes at a byte address.
+__device__ __forceinline__ void lds_write_f32x4(uint32_t addr, f32x4_t v) {
+  typedef __attribute__((address_space(3))) f32x4_t* lds_ptr_t;
+  *(lds_ptr_t)(uintptr_t)addr = v;
+}
+__device__ __forceinline__ void lds_write_bf16x8(uint32_t addr, bf16x8_t v) {
+  typedef __attribute__((address_space(3))) bf16x8_t* lds_ptr_t;
+  *(lds_ptr_t)(uintptr_t)addr = v;
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j receives,

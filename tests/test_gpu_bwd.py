@@ -46,6 +46,8 @@ SMALL = [
     (1, 8, 256, 256, 128, True),     # head count on the XCD grouping
     (1, 8, 192, 448, 64, False),     # XCD grouping, non-causal, Tk > Tq
     (1, 2, 1024, 1024, 128, True),   # many tiles
+    (1, 2, 600, 700, 128, True),     # several 256-query blocks, ragged, diagonal offset
+    (2, 1, 513, 513, 64, False),     # two 256-query blocks plus one row
 ]
 
 
