@@ -14,10 +14,10 @@
 //   * fa_bwd_dkdv: one workgroup of 8 waves per (128-key block, head); each lane owns one key.
 //     Q, dO and the per-row L, D stream through LDS in 32-row tiles; K and V stay in registers
 //     as MFMA B operands.  The two waves on a SIMD own the same 32 keys and split the work: one
-//     computes S = Q K^T, P, dS and dK^T += Q^T dS, the other dP = dO V^T and dV^T += dO^T P;
-//     they exchange P and dP - D through LDS.  dO^T and Q^T come from the transposing LDS read
-//     (ds_read_b64_tr_b16) of the same row-major tiles.  No atomics: every key's dK and dV are
-//     finished by one workgroup.
+//     computes S = Q K^T, P and dV^T += dO^T P, the other dP = dO V^T, dS and dK^T += Q^T dS;
+//     P goes from the first to the second through LDS.  dO^T and Q^T come from the transposing
+//     LDS read (ds_read_b64_tr_b16) of the same row-major tiles.  No atomics: every key's dK
+//     and dV are finished by one workgroup.
 //   * fa_bwd_dq: one workgroup of 8 waves per (256-query block, head); each lane owns one query.
 //     K and V stream through LDS; S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
 //     dQ^T += K^T dS^T with K^T from the transposing read.  The two gradient kernels share no
@@ -308,38 +308,37 @@ __device__ __forceinline__ void wait_tile(int need, int last) {
 // ---------------------------------------------------------------------------------------------
 // dK, dV: one workgroup of 8 waves per (128-key block, head), lane = key; query tiles of 32 rows.
 // Waves w and w + 4 (which share a SIMD) own the same 32 keys and split the work: wave w (role K)
-// holds the K rows and computes S, P, dS and dK; wave w + 4 (role V) holds the V rows and
-// computes dP - D and dV.  They exchange P (bf16, the operand of dV) and dP - D (fp32) through
-// LDS, double-buffered by tile parity.  Each role holds half of a key block's state, so two
-// waves fit per SIMD and one's LDS reads and vector work overlap the other's MFMAs.
-//   role K, step s: dK += Q^T dS of tile s - 1, with P and dS of tile s (from S, computed in the
-//     step before, and dP - D of tile s from role V) scheduled between its MFMAs; then S of
-//     tile s + 1.  P of tile s goes to LDS.
-//   role V, step s: dP - D of tile s + 1 (the accumulator starts from -D), then dV += dO^T P of
-//     tile s - 1 (P from LDS); dP - D of tile s + 1 goes to LDS.
-// Both roles end every step at the same barrier, which publishes the exchanged tiles.
+// holds the K rows and computes S, P and dV; wave w + 4 (role V) holds the V rows and computes
+// dP - D, dS and dK.  P goes from role K to role V through LDS (fp32, double-buffered by tile
+// parity).  Each role holds half of a key block's state, so two waves fit per SIMD and one's LDS
+// reads and vector work overlap the other's MFMAs.
+//   role K, step s: dV += dO^T P of tile s - 1, with P of tile s (from S, computed in the step
+//     before) scheduled between its MFMAs and stored to LDS; then S of tile s + 1.
+//   role V, step s: dK += Q^T dS of tile s - 2, with dS of tile s - 1 (P from role K, dP - D
+//     from the step before) scheduled between its MFMAs; then dP - D of tile s (the accumulator
+//     starts from -D).
+// Both roles end every step at the same barrier, which publishes P; role V runs one step behind
+// role K, so both run steps -1 .. nt + 1 (role K's last one is empty).
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreadsK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int R = 32;        // query rows per streamed tile (one 32-row MFMA block)
-  constexpr int NST = 6;       // LDS stages
-  constexpr int AHEAD = 4;     // step s requests tile s + AHEAD
+  constexpr int NST = 6;       // LDS stages: tiles s - 2 .. s + 1 in use, two in flight
+  constexpr int AHEAD = 3;     // step s requests tile s + AHEAD
   constexpr int kRing = 4;     // MFMA operands in flight
   constexpr int NS = D / 16;   // k-steps over d
   constexpr int ND = D / 32;   // 32-row blocks of dK^T / dV^T
   constexpr int NA = NS;       // S (or dP) MFMAs per tile
-  constexpr int NC = 2 * ND;   // dK^T (or dV^T) MFMAs per tile (two 16-query k-steps)
+  constexpr int NC = 2 * ND;   // dV^T (or dK^T) MFMAs per tile (two 16-query k-steps)
   // Staging: every wave issues the same number of 1 KB loads per tile.  d = 128: each wave loads
   // one piece of Q and one of dO; d = 64 (four pieces per tile): waves 0-3 load Q, 4-7 load dO.
   constexpr bool SPLIT = BTile<D, R, 4>::LOADS < kWavesK;
   using T = BTile<D, R, SPLIT ? 4 : kWavesK>;
-  constexpr int LDS_LD = 64;   // floats of L2 (and of -D) per stage (one 64-lane load)
-  constexpr uint32_t XB = 16u * 64u * 4u;   // dP - D of one tile and wave pair: 4 x 64 x 16 B
-  constexpr uint32_t PB = 16u * 64u * 2u;   // P of one tile and wave pair (bf16): 2 x 64 x 16 B
-  // LDS: Q stages, dO stages, L2 and -D per stage, then the exchange buffers [pair][parity].
+  constexpr int LDS_LD = 64;   // floats of L2 (or of -D) per stage (one 64-lane load)
+  constexpr uint32_t PF = 16u * 64u * 4u;   // P of one tile and wave pair: 4 x 64 lanes x 16 B
+  // LDS: Q stages, dO stages, L2 and -D per stage, then P [pair][parity].
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
-  __shared__ __attribute__((aligned(1024))) float lds_x[4 * 2 * XB / 4];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_p[4 * 2 * PB / 2];
+  __shared__ __attribute__((aligned(1024))) float lds_p[4 * 2 * PF / 4];
   __shared__ __attribute__((aligned(256))) float lds_ld[2 * NST * LDS_LD];
   const uint32_t lq = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t ldo = lq + NST * T::BYTES;
@@ -349,13 +348,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pr = wave & 3;     // wave pair
+  const bool role_k = wave < 4;
   const int g = lane >> 5;
   const Lanes<D, R, SPLIT ? 4 : kWavesK> ln(SPLIT ? pr : wave, lane);
-  // this lane's slots of the pair's exchange buffers (parity and part add immediates)
-  const uint32_t xb =
-      (uint32_t)reinterpret_cast<uintptr_t>(lds_x) + (uint32_t)pr * (2 * XB) + 16u * lane;
-  const uint32_t pbb =
-      (uint32_t)reinterpret_cast<uintptr_t>(lds_p) + (uint32_t)pr * (2 * PB) + 16u * lane;
+  // this lane's slot of the pair's P buffers (parity and part add immediates)
+  const uint32_t pfb =
+      (uint32_t)reinterpret_cast<uintptr_t>(lds_p) + (uint32_t)pr * (2 * PF) + 16u * lane;
 
   int bh, blk;
   block_of(p, false, bh, blk);
@@ -370,33 +368,32 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const u32x4_t rq = rsrc_words(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
   const u32x4_t rdo =
       rsrc_words(p.dout + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
-  const u32x4_t rl = rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
-  const u32x4_t rd = rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
+  // role K stages L2 (for P), role V stages -D (the dP seed); four identical copies each
+  const u32x4_t rld = role_k ? rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u)
+                             : rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
+  const uint32_t lld = role_k ? ll : ld;
   auto request = [&](int it) {   // tile t0 + it into stage it % NST
     const int st = it % NST;
     const uint32_t g0 = (uint32_t)(t0 + it) * (R * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
       if (SPLIT) {
-        const bool qw = wave < 4;
-        lds_dma16(qw ? rq : rdo, (qw ? lq : ldo) + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+        lds_dma16(role_k ? rq : rdo, (role_k ? lq : ldo) + st * T::BYTES + ln.dma_l[i],
+                  g0 + ln.dma_g[i]);
       } else {
         lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
         lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
       }
     }
-    // every wave writes the same 64 values of L2 and -D from the tile's first row on
-    // (identical data, so the copies agree; the tile uses the first 32)
-    const uint32_t r0 = (uint32_t)((t0 + it) * R + lane) * 4u;
-    lds_dma4(rl, ll + st * (LDS_LD * 4), r0);
-    lds_dma4(rd, ld + st * (LDS_LD * 4), r0);
+    // 64 values from the tile's first row on (the tile uses the first 32)
+    lds_dma4(rld, lld + st * (LDS_LD * 4), (uint32_t)((t0 + it) * R + lane) * 4u);
   };
-  constexpr int PER = (SPLIT ? 1 : 2) * T::LPW + 2;   // vector-memory operations per tile
+  constexpr int PER = (SPLIT ? 1 : 2) * T::LPW + 1;   // vector-memory operations per tile
 
   // K (role K) or V (role V) rows of this lane's key as B operands (k = 8 columns per half).
   bf16x8_t kvf[NS];
   {
-    const uint16_t* src = wave < 4 ? p.k : p.v;
+    const uint16_t* src = role_k ? p.k : p.v;
     const __amdgpu_buffer_rsrc_t rkv =
         make_rsrc(src + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
 #pragma unroll
@@ -408,34 +405,33 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and the K/V rows)
   __syncthreads();
 
-  f32x16_t acc[ND];   // dK^T (role K) or dV^T (role V)
+  f32x16_t acc[ND];   // dV^T (role K) or dK^T (role V)
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = f32x16_t{};
   bf16x8_t ring[kRing];
+  const Region<D> rQ(lq, ln.row_off, ln.tr_off), rO(ldo, ln.row_off, ln.tr_off);
 
-  if (wave < 4) {
+  if (role_k) {
     // ------------------------------- role K -------------------------------
     // P is zeroed for queries below thr: keys past the end see nothing; causal keys see
     // queries from key - off on.  thr4: thr relative to the first query this lane holds.
     const int thr4 = key >= p.Tk ? (1 << 30) : (CAUSAL ? key - off - 4 * g : -(1 << 30));
-    f32x16_t sacc;                // S of the next tile (32 queries x this key)
-    bf16x8_t dsb[2][2];           // [tile parity][k-step]: dS as C-part operands
-    const Region<D> rQ(lq, ln.row_off, ln.tr_off);
-    // vector instructions per C-part MFMA: about 6 per score, 16 scores per lane
-    constexpr int VPM = 12;
+    f32x16_t sacc;         // S of the next tile (32 queries x this key)
+    bf16x8_t pb[2][2];     // [tile parity][k-step]: P as C-part operands
+    constexpr int VPM = 9;   // vector instructions per C-part MFMA (about 4.5 per score)
     auto step = [&](auto parts, auto stage, int s) {
       using PT = decltype(parts);
       constexpr int ST = decltype(stage)::value;
       constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
       constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-      using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 8 : 0, PT::c, next, kRing>;
+      using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 4 : 0, PT::c, next, kRing>;
       constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
       constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
       constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
       constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // parities (NST is even)
       asm volatile("" : "+s"(s));
       if (s + AHEAD < nt) request(s + AHEAD);
-      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rQ.tr_opnd(so, i % ND, i / ND); };
+      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rO.tr_opnd(so, i % ND, i / ND); };
       auto opnd = [&](int i) -> bf16x8_t {
         if (i < nc) return c_opnd(so_c, i);
         return rQ.row_opnd(so_a, 0, i - nc);
@@ -445,27 +441,24 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
       }
       if constexpr (PT::v) {
-        f32x4_t L4[4], X4[4];
+        f32x4_t L4[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 4; ++a)
           L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
-          X4[a] = lds_read_f32x4(xb + PV * XB + 1024u * a);
-        }
         const int lt = thr4 - (t0 + s) * R;
-        f32x16_t ds;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int a = i >> 2, e = i & 3;
           float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
           if (8 * a + e < lt) pv = 0.f;
           sacc[i] = pv;
-          ds[i] = pv * X4[a][e];
         }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          lds_write_bf16x8(pbb + PV * PB + 1024u * ks, pack_kstep(sacc, ks));
-          dsb[PV][ks] = pack_kstep(ds, ks);
-        }
+        for (int a = 0; a < 4; ++a)
+          lds_write_f32x4(pfb + PV * PF + 1024u * a,
+                          f32x4_t{sacc[4 * a], sacc[4 * a + 1], sacc[4 * a + 2], sacc[4 * a + 3]});
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pb[PV][ks] = pack_kstep(sacc, ks);
       }
 #pragma unroll
       for (int i = 0; i < S::n; ++i) {
@@ -475,18 +468,17 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         else if (next)
           ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
         if (i < nc) {
-          acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
+          acc[i % ND] = mfma_32x32x16(a, pb[PC][i / ND], acc[i % ND]);
         } else {
           const int j = i - nc;
           sacc = mfma_32x32x16(a, kvf[j], j == 0 ? f32x16_t{} : sacc);
         }
       }
       sched_pattern<S>();
-      // the next step's A part reads tile s + 2
+      // the next step reads tile s + 2 (role K's S)
       wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
       __syncthreads();
     };
-    // steps -1 .. nt (see the pipeline above)
     step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
     step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
     {
@@ -501,72 +493,86 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         step(P{}, Stage<0>{}, s); if (++s > nt) break;
       }
     }
+    step(Parts<false, false, false, false>{}, Stage<0>{}, nt + 1);   // role V's last step
   } else {
     // ------------------------------- role V -------------------------------
-    const Region<D> rO(ldo, ln.row_off, ln.tr_off);
-    f32x16_t dpacc;   // dP - D of the next tile
+    f32x16_t dpacc;        // dP - D of tile s (kept for the dS of the next step)
+    bf16x8_t dsb[2][2];    // [tile parity][k-step]: dS as C-part operands
+    constexpr int VPM = 3;   // vector instructions per C-part MFMA (1.5 per score)
     auto step = [&](auto parts, auto stage, int s) {
       using PT = decltype(parts);
       constexpr int ST = decltype(stage)::value;
-      constexpr int nc = PT::c ? NC : 0;
-      using S = StepSeq<nc, NA, 0, PT::c ? 6 : 4, false, false, kRing, true>;
-      constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
-      constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
-      constexpr int PX = (ST + 1) & 1;   // parity of tiles s - 1 and s + 1
+      constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+      constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+      using S = StepSeq<nc, na, PT::v ? VPM : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next,
+                        kRing>;
+      constexpr uint32_t so_c = ((ST + NST - 2) % NST) * T::BYTES;   // tile s - 2
+      constexpr uint32_t so_n = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+      constexpr uint32_t so_a = ST * T::BYTES;                       // tile s
+      constexpr int PC = ST & 1, PV = (ST + 1) & 1;   // parities of tiles s - 2 and s - 1
       asm volatile("" : "+s"(s));
       if (s + AHEAD < nt) request(s + AHEAD);
+      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rQ.tr_opnd(so, i % ND, i / ND); };
       auto opnd = [&](int i) -> bf16x8_t {
-        if (i < NA) return rO.row_opnd(so_a, 0, i);
-        const int k = i - NA;
-        return rO.tr_opnd(so_c, k % ND, k / ND);
+        if (i < nc) return c_opnd(so_c, i);
+        return rO.row_opnd(so_a, 0, i - nc);
       };
+      if constexpr (!PT::c) {
 #pragma unroll
-      for (int i = 0; i < kRing; ++i) ring[i] = opnd(i);
+        for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+      }
+      if constexpr (PT::v) {
+        // dS of tile s - 1: P from role K times dP - D
+        f32x4_t P4[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) P4[a] = lds_read_f32x4(pfb + PV * PF + 1024u * a);
+        f32x16_t ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = P4[i >> 2][i & 3] * dpacc[i];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dsb[PV][ks] = pack_kstep(ds, ks);
+      }
       // the dP accumulator starts from -D of the tile's rows
       f32x16_t nd0;
+      if constexpr (PT::a) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4_t v4 = lds_read_f32x4(ld + ((ST + 1) % NST) * (LDS_LD * 4) +
-                                          4u * (uint32_t)(8 * a + 4 * g));
+        for (int a = 0; a < 4; ++a) {
+          const f32x4_t v4 = lds_read_f32x4(ld + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
-      }
-      bf16x8_t pv[2];   // P of tile s - 1 from role K
-      if constexpr (PT::c) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pv[ks] = lds_read_bf16x8(pbb + PX * PB + 1024u * ks);
+          for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
+        }
       }
 #pragma unroll
       for (int i = 0; i < S::n; ++i) {
         const bf16x8_t a = ring[i % kRing];
-        if (i + kRing < S::n) ring[i % kRing] = opnd(i + kRing);
-        if (i < NA) {
-          dpacc = mfma_32x32x16(a, kvf[i], i == 0 ? nd0 : dpacc);
+        if (i + kRing < S::n)
+          ring[i % kRing] = opnd(i + kRing);
+        else if (next)
+          ring[i % kRing] = c_opnd(so_n, i + kRing - S::n);
+        if (i < nc) {
+          acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
         } else {
-          const int k = i - NA;
-          acc[k % ND] = mfma_32x32x16(a, pv[k / ND], acc[k % ND]);
+          const int j = i - nc;
+          dpacc = mfma_32x32x16(a, kvf[j], j == 0 ? nd0 : dpacc);
         }
       }
       sched_pattern<S>();
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        lds_write_f32x4(xb + PX * XB + 1024u * a,
-                        f32x4_t{dpacc[4 * a], dpacc[4 * a + 1], dpacc[4 * a + 2], dpacc[4 * a + 3]});
       wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
       __syncthreads();
     };
-    step(Parts<false, false, true, false>{}, Stage<NST - 1>{}, -1);
+    step(Parts<false, false, false, false>{}, Stage<NST - 1>{}, -1);
     step(Parts<false, false, true, false>{}, Stage<0>{}, 0);
+    step(Parts<false, true, true, false>{}, Stage<1>{}, 1);
     {
-      using P = Parts<true, false, true, false>;
-      int s = 1;
+      using P = Parts<true, true, true, false>;
+      int s = 2;
       for (;;) {
-        step(P{}, Stage<1>{}, s); if (++s > nt) break;
-        step(P{}, Stage<2>{}, s); if (++s > nt) break;
-        step(P{}, Stage<3>{}, s); if (++s > nt) break;
-        step(P{}, Stage<4>{}, s); if (++s > nt) break;
-        step(P{}, Stage<5>{}, s); if (++s > nt) break;
-        step(P{}, Stage<0>{}, s); if (++s > nt) break;
+        step(P{}, Stage<2>{}, s); if (++s > nt + 1) break;
+        step(P{}, Stage<3>{}, s); if (++s > nt + 1) break;
+        step(P{}, Stage<4>{}, s); if (++s > nt + 1) break;
+        step(P{}, Stage<5>{}, s); if (++s > nt + 1) break;
+        step(P{}, Stage<0>{}, s); if (++s > nt + 1) break;
+        step(P{}, Stage<1>{}, s); if (++s > nt + 1) break;
       }
     }
   }
@@ -574,8 +580,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
   if (key < p.Tk) {
     const size_t row = ((size_t)bh * (size_t)p.Tk + (size_t)key) * D;
-    void* dst = wave < 4 ? p.dk : p.dv;
-    const float sc = wave < 4 ? p.scale : 1.f;
+    void* dst = role_k ? p.dv : p.dk;
+    const float sc = role_k ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
