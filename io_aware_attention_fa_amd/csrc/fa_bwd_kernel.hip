@@ -416,14 +416,25 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // P is zeroed for queries below thr: keys past the end see nothing; causal keys see
     // queries from key - off on.  thr4: thr relative to the first query this lane holds.
     const int thr4 = key >= p.Tk ? (1 << 30) : (CAUSAL ? key - off - 4 * g : -(1 << 30));
+    // Tiles from s_free on need no mask (wave-uniform): no key of this wave is past the end,
+    // and the tile starts at or below the diagonal of this wave's last key.
+    const int kw0 = blk * kOwnK + pr * 32;
+    int s_free = 0;
+    if (kw0 + 31 >= p.Tk) {
+      s_free = INT32_MAX;
+    } else if (CAUSAL) {
+      const int x = kw0 + 31 - off;   // the first query that sees every key of this wave
+      s_free = x <= 0 ? 0 : (x + R - 1) / R - t0;
+    }
     f32x16_t sacc;         // S of the next tile (32 queries x this key)
     bf16x8_t pb[2][2];     // [tile parity][k-step]: P as C-part operands
-    constexpr int VPM = 9;   // vector instructions per C-part MFMA (about 4.5 per score)
     auto step = [&](auto parts, auto stage, int s) {
       using PT = decltype(parts);
       constexpr int ST = decltype(stage)::value;
       constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
       constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+      // vector instructions per C-part MFMA: about 4.5 per score with the mask, 2.5 without
+      constexpr int VPM = PT::m ? 9 : 5;
       using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 4 : 0, PT::c, next, kRing>;
       constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
       constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
@@ -450,7 +461,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         for (int i = 0; i < 16; ++i) {
           const int a = i >> 2, e = i & 3;
           float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
-          if (8 * a + e < lt) pv = 0.f;
+          if (PT::m && 8 * a + e < lt) pv = 0.f;
           sacc[i] = pv;
         }
 #pragma unroll
@@ -482,16 +493,21 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
     step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
     {
-      using P = Parts<true, true, true, true>;
+      // steps 1 .. nt: whole chains of the NST stage variants with the mask while a chain may
+      // hold a tile that needs it, then chains without (each chain left after step nt)
       int s = 1;
-      for (;;) {
-        step(P{}, Stage<1>{}, s); if (++s > nt) break;
-        step(P{}, Stage<2>{}, s); if (++s > nt) break;
-        step(P{}, Stage<3>{}, s); if (++s > nt) break;
-        step(P{}, Stage<4>{}, s); if (++s > nt) break;
-        step(P{}, Stage<5>{}, s); if (++s > nt) break;
-        step(P{}, Stage<0>{}, s); if (++s > nt) break;
-      }
+      auto chain = [&](auto parts) {
+        step(parts, Stage<1>{}, s); if (++s > nt) return true;
+        step(parts, Stage<2>{}, s); if (++s > nt) return true;
+        step(parts, Stage<3>{}, s); if (++s > nt) return true;
+        step(parts, Stage<4>{}, s); if (++s > nt) return true;
+        step(parts, Stage<5>{}, s); if (++s > nt) return true;
+        step(parts, Stage<0>{}, s); if (++s > nt) return true;
+        return false;
+      };
+      bool fin = false;
+      while (!fin && s < s_free) fin = chain(Parts<true, true, true, true>{});
+      while (!fin) fin = chain(Parts<true, true, true, false>{});
     }
     step(Parts<false, false, false, false>{}, Stage<0>{}, nt + 1);   // role V's last step
   } else {
@@ -610,8 +626,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int ND = D / 32;
   constexpr int NA = 2 * KB * NS;   // S^T and dP^T MFMAs per tile
   constexpr int NC = ND * NK;       // dQ^T MFMAs per tile
-  // vector instructions per C-part MFMA: about 6.5 per score, 16 * KB scores per lane
-  constexpr int VPM = (KB * 16 * 13 / 2 + NC - 1) / NC;
+  // vector instructions per C-part MFMA: about 6.5 per score with the mask and 4.5 without,
+  // 16 * KB scores per lane
+  constexpr int VPM_M = (KB * 16 * 13 / 2 + NC - 1) / NC;
+  constexpr int VPM_U = (KB * 16 * 9 / 2 + NC - 1) / NC;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t lv = lk + NST * T::BYTES;
@@ -631,6 +649,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
   // first key this lane holds in a tile
   const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
   const int lim4 = lim - 4 * g;
+  // Tiles before s_mask need no mask (wave-uniform): their last key is within the limit of
+  // this wave's first query.
+  const int lim_w = CAUSAL ? min(p.Tk - 1, qw0 + off) : p.Tk - 1;
+  const int s_mask = (lim_w + 1) / R;
 
   // Q and dO rows of this lane's query as B operands, and its L2 and -D.
   bf16x8_t qf[NS], dof[NS];
@@ -684,7 +706,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int ST = decltype(stage)::value;
     constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
     constexpr bool next = PT::v;
-    using S = StepSeq<nc, na, PT::v ? VPM : 0, 0, PT::c, next, kRing>;
+    using S = StepSeq<nc, na, PT::v ? (PT::m ? VPM_M : VPM_U) : 0, 0, PT::c, next, kRing>;
     // s as an opaque scalar: otherwise the optimiser keeps a per-lane copy of each value derived
     // from it for every stage variant of the chain
     asm volatile("" : "+s"(s));
@@ -710,7 +732,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
-          if (32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
+          if (PT::m && 32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
           dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
         }
 #pragma unroll
@@ -742,21 +764,26 @@ void fa_bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
   step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
-  // steps 1 .. nt: a chain of the NST stage variants, left after step nt (every step applies
-  // the mask: two more vector instructions per score, and one code path per stage)
+  // steps 1 .. nt: a chain of the NST stage variants, left after step nt; each step in a masked
+  // or an unmasked variant (the mask costs two vector instructions per score)
   {
-    using P = Parts<true, true, true, true>;
+    // whole chains of the NST stage variants without the mask while every step of a chain is
+    // before s_mask, then chains with it (each chain left after step nt)
     int s = 1;
-    for (;;) {
-      step(P{}, Stage<1>{}, s); if (++s > nt) break;
-      step(P{}, Stage<2>{}, s); if (++s > nt) break;
-      step(P{}, Stage<3>{}, s); if (++s > nt) break;
-      step(P{}, Stage<4>{}, s); if (++s > nt) break;
-      step(P{}, Stage<5>{}, s); if (++s > nt) break;
-      step(P{}, Stage<6>{}, s); if (++s > nt) break;
-      step(P{}, Stage<7>{}, s); if (++s > nt) break;
-      step(P{}, Stage<0>{}, s); if (++s > nt) break;
-    }
+    auto chain = [&](auto parts) {
+      step(parts, Stage<1>{}, s); if (++s > nt) return true;
+      step(parts, Stage<2>{}, s); if (++s > nt) return true;
+      step(parts, Stage<3>{}, s); if (++s > nt) return true;
+      step(parts, Stage<4>{}, s); if (++s > nt) return true;
+      step(parts, Stage<5>{}, s); if (++s > nt) return true;
+      step(parts, Stage<6>{}, s); if (++s > nt) return true;
+      step(parts, Stage<7>{}, s); if (++s > nt) return true;
+      step(parts, Stage<0>{}, s); if (++s > nt) return true;
+      return false;
+    };
+    bool fin = false;
+    while (!fin && s + NST <= s_mask) fin = chain(Parts<true, true, true, false>{});
+    while (!fin) fin = chain(Parts<true, true, true, true>{});
   }
 
   if (qrow < p.Tq) {
