@@ -512,6 +512,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     step(Parts<false, false, false, false>{}, Stage<0>{}, nt + 1);   // role V's last step
   } else {
     // ------------------------------- role V -------------------------------
+    // (fewer live registers than role K: a deeper operand ring at d = 128)
+    constexpr int kRingV = D == 128 ? 8 : kRing;
+    bf16x8_t ringv[kRingV];
     f32x16_t dpacc;        // dP - D of tile s (kept for the dS of the next step)
     bf16x8_t dsb[2][2];    // [tile parity][k-step]: dS as C-part operands
     constexpr int VPM = 3;   // vector instructions per C-part MFMA (1.5 per score)
@@ -521,7 +524,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
       constexpr bool next = PT::v;   // the next step (if any) starts with a C part
       using S = StepSeq<nc, na, PT::v ? VPM : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next,
-                        kRing>;
+                        kRingV>;
       constexpr uint32_t so_c = ((ST + NST - 2) % NST) * T::BYTES;   // tile s - 2
       constexpr uint32_t so_n = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
       constexpr uint32_t so_a = ST * T::BYTES;                       // tile s
@@ -535,7 +538,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       };
       if constexpr (!PT::c) {
 #pragma unroll
-        for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+        for (int i = 0; i < kRingV && i < S::n; ++i) ringv[i] = opnd(i);
       }
       if constexpr (PT::v) {
         // dS of tile s - 1: P from role K times dP - D
@@ -560,11 +563,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < S::n; ++i) {
-        const bf16x8_t a = ring[i % kRing];
-        if (i + kRing < S::n)
-          ring[i % kRing] = opnd(i + kRing);
+        const bf16x8_t a = ringv[i % kRingV];
+        if (i + kRingV < S::n)
+          ringv[i % kRingV] = opnd(i + kRingV);
         else if (next)
-          ring[i % kRing] = c_opnd(so_n, i + kRing - S::n);
+          ringv[i % kRingV] = c_opnd(so_n, i + kRingV - S::n);
         if (i < nc) {
           acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
         } else {
