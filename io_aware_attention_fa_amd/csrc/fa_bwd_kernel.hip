@@ -222,17 +222,19 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 //   A: the score-side products (S and dP) of the tile, from row operands in LDS;
 //   V: the elementwise part, P = exp2(S * scale * log2 e - L2), dS = P (dP - D), rounded to bf16;
 //   C: the gradient products that consume P and dS, from transposed operands in LDS.
-// Step s runs C of tile s - 1 with V of tile s scheduled between its MFMAs (the vector
-// instructions issue while the matrix core works), then A of tile s + 1; V of tile s
-// reads the score registers that A filled in the step before.  The bf16 P / dS operands are
-// double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring of
-// registers, each read issued as many MFMAs ahead of its use as the ring holds, and the ring
-// runs across steps: the last MFMAs of step s read the first operands of step s + 1 (C operands
-// of tile s, resident), before the barrier that ends the step.  Tiles are loaded AHEAD steps ahead into a ring of NST
-// stages; the stage of every step is a compile-time constant (the steady-state loop dispatches
-// on s % NST), so that all LDS addresses are per-lane registers plus immediates.  The last two
-// steps run all three parts: their V and A parts read stages holding stale tiles and produce
-// values that are never used.
+// A wave's step s runs C of an earlier tile with V of a later one scheduled between its MFMAs
+// (the vector instructions issue while the matrix core works), then A of the next tile; V reads
+// the score registers that A filled in the step before.  (dQ: C of tile s - 1, V of s, A of
+// s + 1; the two roles of the dK/dV kernel are listed there.)  The bf16 operands that V makes
+// for C are double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring
+// of registers, each read issued as many MFMAs ahead of its use as the ring holds; where the
+// next step starts with a C part the ring runs across steps: the last MFMAs of step s read the
+// first operands of step s + 1 (resident tiles) before the barrier that ends the step.  Tiles
+// are loaded AHEAD steps ahead into a ring of NST stages; the stage of every step is a
+// compile-time constant (the steady state is a chain of the NST stage variants, left after the
+// last step), so that all LDS addresses are per-lane registers plus immediates.  The last steps
+// run every part: their V and A parts read stages holding stale tiles and produce values that
+// are never used.
 
 // A step's MFMA stream: NC C-part MFMAs (two transposing reads each), then NA A-part MFMAs (one
 // read each), or the A part first if AFIRST.  PRE: the ring arrived preloaded; NEXT: the last
@@ -556,7 +558,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       if constexpr (PT::a) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const f32x4_t v4 = lds_read_f32x4(ld + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
+          const f32x4_t v4 =
+              lds_read_f32x4(ld + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
 #pragma unroll
           for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
         }
