@@ -368,8 +368,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        eprint("bench.py measures one GPU: this build has no multi-GPU path (every GPU box has one "
-               "GPU). Run with --gpus 1.")
+        eprint("bench.py measures a single GPU; runs on several GPUs are not supported. "
+               "Run with --gpus 1.")
         sys.exit(2)
 
     import torch

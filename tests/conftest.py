@@ -37,7 +37,7 @@ def fa_lib():
 @pytest.fixture(scope="session")
 def gpu(fa_lib):
     if not _gpu_available():
-        pytest.fail("GPU tests need a visible MI355X; run them with -m gpu on a GPU box")
+        pytest.fail("GPU tests need a visible MI355X (gfx950); run them with -m gpu on a machine that has one")
     import torch
     torch.cuda.init()
     return fa_lib

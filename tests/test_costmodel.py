@@ -98,7 +98,7 @@ def test_lesson_numbers():
     assert round(P / 32 / 3.35e12 * 1e3, 2) == g["saved_hbm_ms_approx"]
 
 
-def test_north_star_flop_and_byte_formulas():
+def test_prefill_and_decode_workload_formulas():
     f = cm.attention_flops(8, 32, 4096, 4096, 128, causal=True)
     assert f == pytest.approx(1.0995e12, rel=1e-4)
     assert cm.attention_io_bytes(8, 32, 4096, 4096, 128) == pytest.approx(1.078e9, rel=1e-3)
