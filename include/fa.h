@@ -176,6 +176,30 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
                float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bwd_strided -- fa_bwd on strided tensors and any head dim (layout variants of the backward).
+ *   Element (b, h, t, c) of each of q, k, v, o, dout, dq, dk, dv is at
+ *   base[b*s[0] + h*s[1] + t*s[2] + c] with that tensor's strides s (elements; the last
+ *   dimension is contiguous), e.g. {T*h*d, d, h*d} for [B][T][h][d] storage.  d_head may be any
+ *   multiple of 8 in [8, 128]: the kernels pad it to 64 or 128 on chip with zeros, which
+ *   changes no product.  lse stays contiguous [B][h][Tq] fp32; dq, dk, dv are bf16.  Same method,
+ *   kernels and precision as fa_bwd; for contiguous tensors with d_head 64 or 128 the results are
+ *   fa_bwd's bit for bit.
+ *   Preconditions: as fa_bwd, with d_head as above, and for each tensor: row stride >= d_head,
+ *   every stride a non-negative multiple of 8 elements, and
+ *   (T + 128) * row_stride * 2 <= FA_MAX_HEAD_BYTES (T = Tq for q, o, dout, dq; Tk for k, v,
+ *   dk, dv).  The outputs must not overlap the inputs, the workspace or each other.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                   const int64_t* q_strides, const int64_t* k_strides,
+                   const int64_t* v_strides, const int64_t* o_strides,
+                   const int64_t* do_strides, const int64_t* dq_strides,
+                   const int64_t* dk_strides, const int64_t* dv_strides,
+                   int causal, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * fa_softmax_rows -- row-wise softmax of a [rows][cols] fp32 matrix, in one pass over HBM.
  *   x [rows][cols] fp32 (in); y [rows][cols] fp32 (out); lse [rows] fp32 (out, natural log) or
  *   NULL.  y_ij = exp(x_ij - m_i) / sum_k exp(x_ik - m_i) with m_i the row max, and
@@ -224,14 +248,22 @@ int fa_gelu_bf16(const void* x, void* y, int64_t n, void* stream);
 int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t rows,
                               int64_t cols, float p, uint64_t seed, uint64_t offset, void* stream);
 
-/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_decode, fa_bwd / fa_bwd_f32,
- * fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16 (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would
- * return. */
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_fwd_strided, fa_decode,
+ * fa_bwd / fa_bwd_f32, fa_bwd_strided, fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16
+ * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return. */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, const void* dq, const void* dk,
                     const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
                     int64_t d_head, int causal, float scale, const void* workspace,
                     size_t workspace_bytes);
+int fa_validate_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const void* dq, const void* dk,
+                            const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
+                            int64_t d_head, const int64_t* q_strides, const int64_t* k_strides,
+                            const int64_t* v_strides, const int64_t* o_strides,
+                            const int64_t* do_strides, const int64_t* dq_strides,
+                            const int64_t* dk_strides, const int64_t* dv_strides, int causal,
+                            float scale, const void* workspace, size_t workspace_bytes);
 int fa_validate_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                     int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
                     int causal, float scale);

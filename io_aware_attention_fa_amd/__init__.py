@@ -19,7 +19,7 @@ from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR
 
 __all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
-           "fa_validate_bwd", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
+           "fa_validate_bwd", "fa_bwd_strided", "fa_validate_bwd_strided", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
            "fa_gelu_bf16", "fa_bias_gelu_dropout_bf16", "fa_validate_gelu",
            "fa_validate_bias_gelu_dropout", "fa_status_str", "fa_last_hip_error", "FaError",
            "LIB_PATH"]
@@ -272,6 +272,65 @@ def fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr,
     return int(_lib.lib.fa_validate_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr,
                                         dk_ptr, dv_ptr, B, h, Tq, Tk, d_head, int(causal),
                                         float(scale), ws_ptr, ws_bytes))
+
+
+def fa_bwd_strided(q, k, v, o, do, lse, *, causal: bool, scale: float | None = None, dq=None,
+                   dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward on strided [B, h, T, d] views (e.g. ``x.transpose(1, 2)`` of a
+    [B, T, h, d] tensor) and any head dim d <= 128 that is a multiple of 8 -> (dq, dk, dv) bf16.
+
+    Every tensor needs a contiguous last dimension; lse is contiguous [B, h, Tq] fp32.  The
+    outputs default to ``torch.empty_like`` of q, k and v (same strides) and may be any such
+    views.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D bf16 tensor")
+    B, h, Tq, d = q.shape
+    Tk = k.shape[2]
+    if (tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d) or
+            tuple(o.shape) != (B, h, Tq, d) or tuple(do.shape) != (B, h, Tq, d)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, o {tuple(o.shape)}, do {tuple(do.shape)}")
+    _check_tensor("lse", lse, torch.float32, 3)
+    if tuple(lse.shape) != (B, h, Tq):
+        raise ValueError(f"lse must be [B, h, Tq], got {tuple(lse.shape)}")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, shape in (("dq", dq, (B, h, Tq, d)), ("dk", dk, (B, h, Tk, d)),
+                           ("dv", dv, (B, h, Tk, d))):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a bf16 view of shape {shape}")
+    if len({t.device for t in (q, k, v, o, do, lse, dq, dk, dv)}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    need = fa_bwd_workspace_size(B, h, Tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8, 1)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = _lib.lib.fa_bwd_strided(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, h, Tq, Tk, d,
+        *(_strides3(n, t) for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do),
+                                        ("dq", dq), ("dk", dk), ("dv", dv))),
+        int(bool(causal)), scale, workspace.data_ptr(), workspace.numel(),
+        _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv
+
+
+def fa_validate_bwd_strided(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr,
+                            B, h, Tq, Tk, d_head, strides, causal, scale, ws_ptr, ws_bytes):
+    """Host-only argument check of fa_bwd_strided (raw addresses; ``strides`` is a sequence of
+    eight 3-sequences or None, for q, k, v, o, do, dq, dk, dv)."""
+    import ctypes
+    arr = [None if s_ is None else (ctypes.c_int64 * 3)(*s_) for s_ in strides]
+    return int(_lib.lib.fa_validate_bwd_strided(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr,
+                                                dq_ptr, dk_ptr, dv_ptr, B, h, Tq, Tk, d_head,
+                                                *arr, int(causal), float(scale), ws_ptr,
+                                                ws_bytes))
 
 
 def fa_softmax_rows(x, *, y=None, lse=None, with_lse: bool = False, stream=None):

@@ -40,6 +40,9 @@ SIGNATURES = {
                           _i64, _int, _f32, _vp, _size, _vp]),
     "fa_validate_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                _i64, _i64, _int, _f32, _vp, _size]),
+    "fa_bwd_strided": (_int, [_vp] * 9 + [_i64] * 5 + [_vp] * 8 + [_int, _f32, _vp, _size, _vp]),
+    "fa_validate_bwd_strided": (_int, [_vp] * 9 + [_i64] * 5 + [_vp] * 8 + [_int, _f32, _vp,
+                                                                            _size]),
     "fa_softmax_rows": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "fa_validate_softmax": (_int, [_vp, _vp, _vp, _i64, _i64]),
     "fa_gelu_f32": (_int, [_vp, _vp, _i64, _vp]),

@@ -54,13 +54,21 @@ constexpr int kWavesQ = 8;    // dQ: two waves per SIMD, 32 own queries each
 constexpr int kOwnQ = 32 * kWavesQ;
 constexpr int kThreadsQ = 64 * kWavesQ;
 
+// Layout of one [B][h][T][d] tensor: element (b, h, t, c) at base[b*sb + h*sh + t*st + c].
+struct Lay {
+  int64_t sb, sh;
+  uint32_t st;
+};
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* o;
   const uint16_t* dout;
-  const float* l2;   // LSE_i * log2(e), [BH][Tq]
-  const float* dd;   // -D_i = -<dO_i, O_i>, [BH][Tq]
+  const float* lse;
+  float* l2;   // LSE_i * log2(e), [BH][Tq] (workspace)
+  float* dd;   // -D_i = -<dO_i, O_i>, [BH][Tq] (workspace)
   void* dq;
   void* dk;
   void* dv;
@@ -68,7 +76,34 @@ struct BwdParams {
   int groups;             // 8: workgroup n works on heads n % 8, n % 8 + 8, ... (XCD-local)
   float c;                // scale * log2(e)
   float scale;
+  // general layouts (used by the GEN variants): heads per batch entry, the true head dim
+  // d <= D (columns d .. D - 1 are zero padding on chip) and each tensor's strides
+  int H, d;
+  Lay lq, lk, lv, lo, ldo, ldq, ldk, ldv;
 };
+
+// A buffer offset beyond every head's range (heads are < 2^31 bytes): loads return zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
+
+// Layout helpers: with GEN = false (contiguous, d = D) they reduce to compile-time strides.
+template <int D, bool GEN>
+__device__ __forceinline__ int64_t head_elem(const BwdParams& p, const Lay& l, int bh, int T) {
+  if (!GEN) return (int64_t)bh * T * D;
+  const int b = __builtin_amdgcn_readfirstlane(bh / p.H);
+  return (int64_t)b * l.sb + (int64_t)(bh - b * p.H) * l.sh;
+}
+template <int D, bool GEN>
+__device__ __forceinline__ uint32_t row_stride(const Lay& l) {
+  return GEN ? l.st : (uint32_t)D;
+}
+// a head's byte range: rows 0 .. T - 1 of stride st, the last one d columns wide
+__device__ __forceinline__ uint32_t head_bytes(int T, uint32_t st, int d) {
+  return ((uint32_t)(T - 1) * st + (uint32_t)d) * 2u;
+}
+// byte offset of the 16 bytes at (row, col) of a head; padding columns read zeros
+__device__ __forceinline__ uint32_t off16(int row, int col, uint32_t st, int d) {
+  return col < d ? ((uint32_t)row * st + (uint32_t)col) * 2u : kPadOffset;
+}
 
 // A streamed tile of ROWS rows of D bf16 and how the W waves of a workgroup load it.
 template <int D, int ROWS, int W>
@@ -101,8 +136,9 @@ template <int D, int ROWS, int W>
 struct Lanes {
   using T = BTile<D, ROWS, W>;
   uint32_t row_off, tr_off;
-  uint32_t dma_l[T::LPW], dma_g[T::LPW];   // LDS / global byte offsets of this wave's loads
-  __device__ __forceinline__ Lanes(int wave, int lane) {
+  uint32_t dma_l[T::LPW];   // LDS byte offsets of this wave's loads
+  int w_, l_;
+  __device__ __forceinline__ Lanes(int wave, int lane) : w_(wave), l_(lane) {
     const int g = lane >> 5, r32 = lane & 31;
     row_off = 2u * (uint32_t)(r32 * D) + 16u * (uint32_t)(g ^ T::f(r32));
     const int x = (lane & 15) >> 2, dh = (lane >> 4) & 1, b = (lane & 3) >> 1;
@@ -110,13 +146,15 @@ struct Lanes {
     const int phys0 = (2 * dh + b) ^ (4 * xr + g);
     tr_off = 2u * (uint32_t)((4 * g + x) * D) + 16u * (uint32_t)phys0 + 8u * (uint32_t)(lane & 1);
 #pragma unroll
-    for (int i = 0; i < T::LPW; ++i) {
-      // load n fills tile rows n*ROWS_PER_LOAD.. : lane l -> row + l / CH, physical chunk l % CH
-      const int nld = wave * T::LPW + i;
-      const int r = nld * T::ROWS_PER_LOAD + lane / T::CH, pc = lane % T::CH;
-      dma_l[i] = (uint32_t)nld * 1024u;
-      dma_g[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ T::f(r)));
-    }
+    for (int i = 0; i < T::LPW; ++i) dma_l[i] = (uint32_t)(wave * T::LPW + i) * 1024u;
+  }
+  // Global byte offset (within a tile of rows of stride st, d real columns) of load i: load n
+  // fills tile rows n*ROWS_PER_LOAD.. : lane l -> row + l / CH, physical chunk l % CH, which
+  // holds the logical chunk the swizzle maps there.
+  __device__ __forceinline__ uint32_t goff(int i, uint32_t st, int d) const {
+    const int nld = w_ * T::LPW + i;
+    const int r = nld * T::ROWS_PER_LOAD + l_ / T::CH, c = (l_ % T::CH) ^ T::f(r);
+    return 8 * c < d ? 2u * ((uint32_t)r * st + 8u * (uint32_t)c) : kPadOffset;
   }
 };
 
@@ -191,29 +229,35 @@ __device__ __forceinline__ void block_of(const BwdParams& p, bool reverse, int& 
 // ---------------------------------------------------------------------------------------------
 // Preprocess: -D_i = -<dO_i, O_i> (fp32 sum of bf16 products) and LSE_i * log2(e).
 // One row per D/8 lanes (16 bytes each); rows = B * h * Tq.
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __restrict__ o,
-                                                          const uint16_t* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          float* __restrict__ l2,
-                                                          float* __restrict__ dd, int64_t rows) {
+template <int D, bool GEN>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p, int64_t rows) {
   constexpr int LPR = D / 8;   // lanes per row
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   float acc = 0.f;
   if (row < rows) {
-    const size_t e = (size_t)row * D + 8 * part;
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(o + e);
-    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(dout + e);
+    int64_t eo, ed;
+    if (!GEN) {
+      eo = ed = row * D + 8 * part;
+    } else {
+      const int bh = (int)(row / p.Tq), t = (int)(row - (int64_t)bh * p.Tq), b = bh / p.H;
+      const int hh = bh - b * p.H;
+      eo = b * p.lo.sb + hh * p.lo.sh + (int64_t)t * p.lo.st + 8 * part;
+      ed = b * p.ldo.sb + hh * p.ldo.sh + (int64_t)t * p.ldo.st + 8 * part;
+    }
+    if (!GEN || 8 * part < p.d) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p.o + eo);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p.dout + ed);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[i]), as_bf16x2(b[i]), acc, false);
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[i]), as_bf16x2(b[i]), acc, false);
+    }
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (row < rows && part == 0) {
-    dd[row] = -acc;
-    l2[row] = lse[row] * kLog2e;
+    p.dd[row] = -acc;
+    p.l2[row] = p.lse[row] * kLog2e;
   }
 }
 
@@ -321,7 +365,7 @@ __device__ __forceinline__ void wait_tile(int need, int last) {
 //     starts from -D).
 // Both roles end every step at the same barrier, which publishes P; role V runs one step behind
 // role K, so both run steps -1 .. nt + 1 (role K's last one is empty).
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
 __global__ __launch_bounds__(kThreadsK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int R = 32;        // query rows per streamed tile (one 32-row MFMA block)
@@ -367,24 +411,34 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwnK - off) / R) : 0;
   const int nt = nqt - t0;
 
-  const u32x4_t rq = rsrc_words(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
-  const u32x4_t rdo =
-      rsrc_words(p.dout + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
+  const int hd = GEN ? p.d : D;   // true head dim
+  const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
+  const u32x4_t rq = rsrc_words(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
+                                head_bytes(p.Tq, st_q, hd));
+  const u32x4_t rdo = rsrc_words(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
+                                 head_bytes(p.Tq, st_do, hd));
+  uint32_t gq[T::LPW], gdo[T::LPW];   // this wave's global load offsets within a tile
+#pragma unroll
+  for (int i = 0; i < T::LPW; ++i) {
+    gq[i] = ln.goff(i, st_q, hd);
+    gdo[i] = ln.goff(i, st_do, hd);
+  }
   // role K stages L2 (for P), role V stages -D (the dP seed); four identical copies each
   const u32x4_t rld = role_k ? rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u)
                              : rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
   const uint32_t lld = role_k ? ll : ld;
   auto request = [&](int it) {   // tile t0 + it into stage it % NST
     const int st = it % NST;
-    const uint32_t g0 = (uint32_t)(t0 + it) * (R * D * 2);
+    const uint32_t g0q = (uint32_t)(t0 + it) * (R * 2u) * st_q;
+    const uint32_t g0d = (uint32_t)(t0 + it) * (R * 2u) * st_do;
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
       if (SPLIT) {
         lds_dma16(role_k ? rq : rdo, (role_k ? lq : ldo) + st * T::BYTES + ln.dma_l[i],
-                  g0 + ln.dma_g[i]);
+                  role_k ? g0q + gq[i] : g0d + gdo[i]);
       } else {
-        lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
-        lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+        lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0q + gq[i]);
+        lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0d + gdo[i]);
       }
     }
     // 64 values from the tile's first row on (the tile uses the first 32)
@@ -396,11 +450,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   bf16x8_t kvf[NS];
   {
     const uint16_t* src = role_k ? p.k : p.v;
+    const Lay& lkv = role_k ? p.lk : p.lv;
+    const uint32_t st = row_stride<D, GEN>(lkv);
     const __amdgpu_buffer_rsrc_t rkv =
-        make_rsrc(src + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+        make_rsrc(src + head_elem<D, GEN>(p, lkv, bh, p.Tk), head_bytes(p.Tk, st, hd));
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      kvf[s] = as_bf16x8(buf_load16(rkv, (uint32_t)(key * D + 16 * s + 8 * g) * 2u));
+      kvf[s] = as_bf16x8(buf_load16(rkv, off16(key, 16 * s + 8 * g, st, hd)));
   }
 
   for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
@@ -601,15 +657,20 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
   if (key < p.Tk) {
-    const size_t row = ((size_t)bh * (size_t)p.Tk + (size_t)key) * D;
+    const Lay& lg = role_k ? p.ldv : p.ldk;
+    const size_t row = (size_t)(head_elem<D, GEN>(p, lg, bh, p.Tk) +
+                                (int64_t)key * row_stride<D, GEN>(lg));
     void* dst = role_k ? p.dv : p.dk;
     const float sc = role_k ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        store4<OUT_F32>(dst, row + 32 * db + 8 * a + 4 * g, sc * acc[db][4 * a],
-                        sc * acc[db][4 * a + 1], sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
+      for (int a = 0; a < 4; ++a) {
+        const int col = 32 * db + 8 * a + 4 * g;
+        if (!GEN || col < hd)
+          store4<OUT_F32>(dst, row + col, sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
+                          sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
+      }
   }
 }
 
@@ -618,7 +679,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 // tiles of 32 rows (d = 128) or 64 rows (d = 64).  The per-wave state fits in half of a SIMD's
 // registers, so the two waves of a SIMD overlap one's LDS reads and vector work with the
 // other's MFMAs.
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
 __global__ __launch_bounds__(kThreadsQ) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int R = D == 128 ? 32 : 64;   // keys per streamed tile
@@ -661,18 +722,19 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int s_mask = (lim_w + 1) / R;
 
   // Q and dO rows of this lane's query as B operands, and its L2 and -D.
+  const int hd = GEN ? p.d : D;   // true head dim
   bf16x8_t qf[NS], dof[NS];
   float l2q = 0.f, ndq = 0.f;
   {
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(p.q + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
-    const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(p.dout + (size_t)bh * (size_t)p.Tq * D, (uint32_t)p.Tq * D * 2u);
+    const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
+                                                head_bytes(p.Tq, st_q, hd));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
+                                                 head_bytes(p.Tq, st_do, hd));
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint32_t o = (uint32_t)(qrow * D + 16 * s + 8 * g) * 2u;
-      qf[s] = as_bf16x8(buf_load16(rq, o));
-      dof[s] = as_bf16x8(buf_load16(rdo, o));
+      qf[s] = as_bf16x8(buf_load16(rq, off16(qrow, 16 * s + 8 * g, st_q, hd)));
+      dof[s] = as_bf16x8(buf_load16(rdo, off16(qrow, 16 * s + 8 * g, st_do, hd)));
     }
     if (qrow < p.Tq) {
       l2q = p.l2[(size_t)bh * p.Tq + qrow];
@@ -684,15 +746,24 @@ void fa_bwd_dq_kernel(BwdParams p) {
   if (CAUSAL) kend = min(p.Tk, min(i0 + kOwnQ, p.Tq) + off);
   const int nt = __builtin_amdgcn_readfirstlane((kend + R - 1) / R);
 
-  const u32x4_t rk = rsrc_words(p.k + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
-  const u32x4_t rv = rsrc_words(p.v + (size_t)bh * (size_t)p.Tk * D, (uint32_t)p.Tk * D * 2u);
+  const uint32_t st_k = row_stride<D, GEN>(p.lk), st_v = row_stride<D, GEN>(p.lv);
+  const u32x4_t rk = rsrc_words(p.k + head_elem<D, GEN>(p, p.lk, bh, p.Tk),
+                                head_bytes(p.Tk, st_k, hd));
+  const u32x4_t rv = rsrc_words(p.v + head_elem<D, GEN>(p, p.lv, bh, p.Tk),
+                                head_bytes(p.Tk, st_v, hd));
+  uint32_t gk[T::LPW], gv[T::LPW];   // this wave's global load offsets within a tile
+#pragma unroll
+  for (int i = 0; i < T::LPW; ++i) {
+    gk[i] = ln.goff(i, st_k, hd);
+    gv[i] = ln.goff(i, st_v, hd);
+  }
   auto request = [&](int it) {
     const int st = it & (NST - 1);
-    const uint32_t g0 = (uint32_t)it * (R * D * 2);
+    const uint32_t g0k = (uint32_t)it * (R * 2u) * st_k, g0v = (uint32_t)it * (R * 2u) * st_v;
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
-      lds_dma16(rk, lk + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
-      lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0 + ln.dma_g[i]);
+      lds_dma16(rk, lk + st * T::BYTES + ln.dma_l[i], g0k + gk[i]);
+      lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0v + gv[i]);
     }
   };
   constexpr int PER = 2 * T::LPW;
@@ -793,34 +864,32 @@ void fa_bwd_dq_kernel(BwdParams p) {
   }
 
   if (qrow < p.Tq) {
-    const size_t row = ((size_t)bh * (size_t)p.Tq + (size_t)qrow) * D;
+    const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
+                                (int64_t)qrow * row_stride<D, GEN>(p.ldq));
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        store4<OUT_F32>(p.dq, row + 32 * db + 8 * a + 4 * g, p.scale * accq[db][4 * a],
-                        p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
-                        p.scale * accq[db][4 * a + 3]);
+      for (int a = 0; a < 4; ++a) {
+        const int col = 32 * db + 8 * a + 4 * g;
+        if (!GEN || col < hd)
+          store4<OUT_F32>(p.dq, row + col, p.scale * accq[db][4 * a],
+                          p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
+                          p.scale * accq[db][4 * a + 3]);
+      }
   }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+Lay to_lay(const int64_t* s3) { return Lay{s3[0], s3[1], (uint32_t)s3[2]}; }
+
+template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
 hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.H * a.Tq;
-  {
-    constexpr int rows_per_block = 256 / (D / 8);
-    const int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL(fa_bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                       a.lse, a.l2, a.dd, rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   BwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<const uint16_t*>(a.o);
   p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
   p.l2 = a.l2;
   p.dd = a.dd;
   p.dq = a.dq;
@@ -832,35 +901,67 @@ hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.groups = (p.BH % 8 == 0) ? 8 : 1;
+  p.H = a.H;
+  p.d = a.d;
+  p.lq = to_lay(a.q_s);
+  p.lk = to_lay(a.k_s);
+  p.lv = to_lay(a.v_s);
+  p.lo = to_lay(a.o_s);
+  p.ldo = to_lay(a.do_s);
+  p.ldq = to_lay(a.dq_s);
+  p.ldk = to_lay(a.dk_s);
+  p.ldv = to_lay(a.dv_s);
+  {
+    const int64_t rows = (int64_t)a.B * a.H * a.Tq;
+    constexpr int rows_per_block = 256 / (D / 8);
+    const int64_t grid = (rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((fa_bwd_prep_kernel<D, GEN>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       p, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     p.nblk = (a.Tk + kOwnK - 1) / kOwnK;
     void* args[] = {&p};
-    const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32>),
-                        dim3(p.BH * p.nblk), dim3(kThreadsK), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32, GEN>),
+        dim3(p.BH * p.nblk), dim3(kThreadsK), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
     p.nblk = (a.Tq + kOwnQ - 1) / kOwnQ;
     void* args[] = {&p};
-    const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, OUT_F32>),
-                        dim3(p.BH * p.nblk), dim3(kThreadsQ), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, OUT_F32, GEN>),
+        dim3(p.BH * p.nblk), dim3(kThreadsQ), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+// GEN = false for contiguous [B][h][T][D] tensors (d = D), else the general-layout kernels.
 template <int D>
 hipError_t launch_d(const BwdLaunch& a, hipStream_t s) {
-  if (a.causal) return a.out_f32 ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
-  return a.out_f32 ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
+  const int64_t H = a.H;
+  auto dense = [&](const int64_t* s3, int64_t T) {
+    return s3[2] == D && s3[1] == T * D && s3[0] == H * T * D;
+  };
+  const bool gen = a.d != D || !dense(a.q_s, a.Tq) || !dense(a.k_s, a.Tk) ||
+                   !dense(a.v_s, a.Tk) || !dense(a.o_s, a.Tq) || !dense(a.do_s, a.Tq) ||
+                   !dense(a.dq_s, a.Tq) || !dense(a.dk_s, a.Tk) || !dense(a.dv_s, a.Tk);
+  if (gen) {   // general layouts: bf16 outputs only
+    if (a.out_f32) return hipErrorInvalidValue;
+    return a.causal ? launch<D, true, false, true>(a, s) : launch<D, false, false, true>(a, s);
+  }
+  if (a.causal)
+    return a.out_f32 ? launch<D, true, true, false>(a, s) : launch<D, true, false, false>(a, s);
+  return a.out_f32 ? launch<D, false, true, false>(a, s) : launch<D, false, false, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream) {
-  if (a.d == 64) return launch_d<64>(a, stream);
+  if (a.d <= 64) return launch_d<64>(a, stream);
   return launch_d<128>(a, stream);
 }
 

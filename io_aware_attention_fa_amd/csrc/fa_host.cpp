@@ -82,13 +82,11 @@ extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, f
 }
 
 namespace {
-int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+// Enqueues the backward; strides s[8][3] of q, k, v, o, dout, dq, dk, dv (validated).
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t h, int64_t Tq,
-               int64_t Tk, int64_t d, int causal, float scale, void* workspace,
-               size_t workspace_bytes, void* stream, bool out_f32) {
-  const int st = fa_validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d, causal, scale,
-                                 workspace, workspace_bytes);
-  if (st != FA_OK) return st;
+               int64_t Tk, int64_t d, const int64_t* const s[8], int causal, float scale,
+               void* workspace, void* stream, bool out_f32) {
   fa::BwdLaunch a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
@@ -99,7 +97,24 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   a.B = static_cast<int>(B); a.H = static_cast<int>(h);
   a.Tq = static_cast<int>(Tq); a.Tk = static_cast<int>(Tk); a.d = static_cast<int>(d);
   a.causal = causal != 0; a.out_f32 = out_f32; a.scale = scale;
+  int64_t* dst[8] = {a.q_s, a.k_s, a.v_s, a.o_s, a.do_s, a.dq_s, a.dk_s, a.dv_s};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) dst[t][i] = s[t][i];
   return map_hip(fa::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t h, int64_t Tq,
+               int64_t Tk, int64_t d, int causal, float scale, void* workspace,
+               size_t workspace_bytes, void* stream, bool out_f32) {
+  const int st = fa_validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d, causal, scale,
+                                 workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  // contiguous [B][h][T][d]
+  const int64_t qs[3] = {h * Tq * d, Tq * d, d}, ks[3] = {h * Tk * d, Tk * d, d};
+  const int64_t* const s[8] = {qs, ks, ks, qs, qs, qs, ks, ks};
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d, s, causal, scale,
+                    workspace, stream, out_f32);
 }
 }  // namespace
 
@@ -118,6 +133,26 @@ extern "C" int fa_bwd_f32(const void* q, const void* k, const void* v, const voi
                           void* stream) {
   return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d_head, causal, scale,
                     workspace, workspace_bytes, stream, true);
+}
+
+extern "C" int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
+                              const int64_t* q_strides, const int64_t* k_strides,
+                              const int64_t* v_strides, const int64_t* o_strides,
+                              const int64_t* do_strides, const int64_t* dq_strides,
+                              const int64_t* dk_strides, const int64_t* dv_strides, int causal,
+                              float scale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const int st = fa_validate_bwd_strided(
+      q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d_head, q_strides, k_strides, v_strides,
+      o_strides, do_strides, dq_strides, dk_strides, dv_strides, causal, scale, workspace,
+      workspace_bytes);
+  if (st != FA_OK) return st;
+  const int64_t* const s[8] = {q_strides,  k_strides,  v_strides,  o_strides,
+                               do_strides, dq_strides, dk_strides, dv_strides};
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d_head, s, causal, scale,
+                    workspace, stream, false);
 }
 
 extern "C" int fa_softmax_rows(const float* x, float* y, float* lse, int64_t rows, int64_t cols,

@@ -47,6 +47,8 @@ struct BwdLaunch {
   bool causal;
   bool out_f32;
   float scale;
+  // element strides (batch, head, row) of each tensor; the last dimension is contiguous
+  int64_t q_s[3], k_s[3], v_s[3], o_s[3], do_s[3], dq_s[3], dk_s[3], dv_s[3];
 };
 
 struct SoftmaxLaunch {

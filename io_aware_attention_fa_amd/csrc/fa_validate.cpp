@@ -142,6 +142,37 @@ extern "C" int fa_validate_bwd(const void* q, const void* k, const void* v, cons
   return FA_OK;
 }
 
+extern "C" int fa_validate_bwd_strided(
+    const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, const void* dq, const void* dk, const void* dv, int64_t B, int64_t h,
+    int64_t Tq, int64_t Tk, int64_t d_head, const int64_t* q_strides, const int64_t* k_strides,
+    const int64_t* v_strides, const int64_t* o_strides, const int64_t* do_strides,
+    const int64_t* dq_strides, const int64_t* dk_strides, const int64_t* dv_strides, int causal,
+    float scale, const void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!strides_ok(q_strides, Tq, d_head, B, h) || !strides_ok(o_strides, Tq, d_head, B, h) ||
+      !strides_ok(do_strides, Tq, d_head, B, h) || !strides_ok(dq_strides, Tq, d_head, B, h) ||
+      !strides_ok(k_strides, Tk, d_head, B, h) || !strides_ok(v_strides, Tk, d_head, B, h) ||
+      !strides_ok(dk_strides, Tk, d_head, B, h) || !strides_ok(dv_strides, Tk, d_head, B, h))
+    return FA_ERR_SHAPE;
+  const int64_t nb = ((Tq > Tk ? Tq : Tk) + 127) / 128;
+  if (B > INT32_MAX / h || B * h > INT32_MAX / nb) return FA_ERR_SHAPE;
+  if (B * h > (int64_t)UINT32_MAX * 16 / Tq) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Tq > Tk) return FA_ERR_CAUSAL_TQ_GT_TK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < fa_bwd_workspace_size(B, h, Tq))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
 extern "C" int fa_validate_softmax(const float* x, const float* y, const float* lse, int64_t rows,
                                    int64_t cols) {
   if (!x || !y) return FA_ERR_NULL;

@@ -237,3 +237,50 @@ def _vs(fa_lib, **kw):
 ])
 def test_validate_fwd_strided(fa_lib, kw, code):
     assert _vs(fa_lib, **kw) == code
+
+
+def _vbs(fa_lib, **kw):
+    qs = (3 * 100 * 80, 80, 3 * 80)   # [B][T][h][d] storage of q, o, do, dq
+    ks = (3 * 120 * 80, 80, 3 * 80)   # ... of k, v, dk, dv
+    a = dict(B=2, h=3, Tq=100, Tk=120, d=80, causal=1, scale=0.1, ws=P, ws_bytes=None,
+             strides=[qs, ks, ks, qs, qs, qs, ks, ks], lse=P, dk=P)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = fa_lib.fa_bwd_workspace_size(2, 3, 100)
+    return fa_lib.fa_validate_bwd_strided(P, P, P, P, P, a["lse"], P, a["dk"], P, a["B"], a["h"],
+                                          a["Tq"], a["Tk"], a["d"], a["strides"], a["causal"],
+                                          a["scale"], a["ws"], a["ws_bytes"])
+
+
+_QS, _KS = (3 * 100 * 80, 80, 3 * 80), (3 * 120 * 80, 80, 3 * 80)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"d": 64, "strides": [(0, 0, 64)] * 8}, 0),
+    ({"d": 8, "strides": [(0, 0, 8)] * 8}, 0),
+    ({"lse": 0}, 1), ({"dk": 0}, 1),
+    ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, _KS, None]}, 2),
+    ({"strides": [_QS, _KS, _KS, _QS, (3 * 100 * 80, 80, 72), _QS, _KS, _KS]}, 2),   # do row < d
+    ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, (3 * 120 * 80, 84, 3 * 80), _KS]}, 2),
+    ({"strides": [_QS, (0, 0, 2**26), _KS, _QS, _QS, _QS, _KS, _KS]}, 2),   # k head > 2^31 B
+    ({"d": 100}, 3), ({"d": 136}, 3), ({"Tq": 121}, 4),
+    ({"lse": P + 2}, 5), ({"dk": P + 8}, 5),
+    ({"causal": 2}, 6), ({"ws_bytes": 16}, 8),
+])
+def test_validate_bwd_strided(fa_lib, kw, code):
+    assert _vbs(fa_lib, **kw) == code
+
+
+def test_invalid_bwd_strided_call_touches_nothing(fa_lib):
+    from io_aware_attention_fa_amd import _lib
+    buf = np.zeros(4096, dtype=np.uint16)
+    out = np.full(4096, 0x7FC1, dtype=np.uint16)
+    lse = np.zeros(64, dtype=np.float32)
+    ws = np.full(4096, 7, dtype=np.uint8)
+    a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, buf, buf, lse, out, out, out)]
+    s3 = (ctypes.c_int64 * 3)(16 * 104, 104, 104)
+    st = _lib.lib.fa_bwd_strided(*a, 1, 1, 16, 16, 100, *([s3] * 8), 0, 0.125,
+                                 ctypes.c_void_p(ws.ctypes.data), ws.nbytes, None)
+    assert st == 3
+    assert np.all(out == 0x7FC1) and np.all(ws == 7)
