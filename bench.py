@@ -238,8 +238,9 @@ def measure_softmax(args, fa, si, torch):
 
 
 def measure_layouts(args, fa, si, cm, torch):
-    """The forward on layout variants: the prefill workload with q, k, v in [B][T][h][d] (strided
-    views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the pages' padding example."""
+    """The forward and the backward on layout variants: the prefill workload with the tensors in
+    [B][T][h][d] (strided views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the pages'
+    padding example."""
     import numpy as np
     peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
     K = args.extra_steps or 20
@@ -273,6 +274,44 @@ def measure_layouts(args, fa, si, cm, torch):
                                "layout": "BTHD strided" if strided else "BHTD contiguous",
                                "flops": flops}}
         del tq, tk, tv
+        torch.cuda.empty_cache()
+    # the backward on the same variants (fa_bwd_strided): [B][T][h][d] inputs and outputs at the
+    # prefill shape, and d_head = 80 contiguous (padded on chip)
+    for key, (B, h, T, d, strided) in {"bwd_bthd": (8, 32, 4096, 128, True),
+                                        "bwd_d80": (8, 20, 4096, 80, False)}.items():
+        wl = si.custom_workload(B, h, T, T, d, True, name=key)
+        q, k, v = si.make_inputs(wl, seed=0)
+        dob = si.make_grad(wl, seed=0)
+        if strided:
+            def lay(bits):
+                return upload(np.ascontiguousarray(bits.transpose(0, 2, 1, 3))).transpose(1, 2)
+        else:
+            lay = upload
+        tq, tk, tv, tdo = lay(q), lay(k), lay(v), lay(dob)
+        del q, k, v, dob
+        to = torch.empty_like(tq)
+        lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
+        fa.fa_fwd_strided(tq, tk, tv, causal=True, scale=wl.scale, o=to, lse=lse)
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, h, T), dtype=torch.uint8, device="cuda")
+        call = lambda: fa.fa_bwd_strided(tq, tk, tv, to, tdo, lse, causal=True, scale=wl.scale,
+                                         dq=dq, dk=dk, dv=dv, workspace=ws)
+        ms = time_calls(torch, call, 3, max(5, K // 4))
+        flops = cm.attention_bwd_flops(B, h, T, T, d, True)
+        tf = flops / (ms * 1e-3) / 1e12
+        eprint(f"[bench] layout {key}: B={B} h={h} T={T} d={d} avg {ms:.4f} ms  {tf:.1f} TFLOP/s "
+               f"(2.5x fwd FLOPs)  {100 * tf / peak:.1f}% of {peak:.0f}")
+        res[key] = {"metric": f"attention backward TFLOP/s (2.5x forward FLOPs), causal, "
+                              f"d_head={d}" + (", [B][T][h][d] tensors" if strided else
+                                               ", padded to 128 on chip"),
+                    "value": tf, "unit": "TFLOP/s", "steps": max(5, K // 4), "warmup": 3,
+                    "avg_ms": ms,
+                    "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                                 "frac": tf / peak, "traffic": None},
+                    "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
+                               "layout": "BTHD strided" if strided else "BHTD contiguous",
+                               "flops": flops}}
+        del tq, tk, tv, tdo, to, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return res
 
