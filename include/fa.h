@@ -112,9 +112,10 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, float scale, void* stream);
 
 /*
- * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
- *   B * h * num_splits * (d_head + 2) fp32 partials (chunk max, denominator, d_head outputs).
- *   Returns 0 for sizes < 1.
+ * fa_decode_workspace_size -- bytes of device workspace fa_decode / fa_decode_strided need:
+ *   B * h * num_splits * (w + 2) fp32 partials (chunk max, denominator, w outputs), where w is
+ *   the width the kernels compute in: 64 for d_head <= 64, 128 for d_head <= 128 (d_head
+ *   itself when larger).  Returns 0 for sizes < 1.
  */
 size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t num_splits);
 
@@ -134,6 +135,24 @@ size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t nu
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
               int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_strided -- fa_decode on strided tensors and any head dim (layout variants).
+ *   Element (b, h, c) of q is q[b*q_strides[0] + h*q_strides[1] + c], likewise o with
+ *   o_strides; element (b, h, t, c) of k is k[b*k_strides[0] + h*k_strides[1] + t*k_strides[2]
+ *   + c], likewise v (strides in elements; the last dimension contiguous), e.g. a [B][Tk][h][d]
+ *   KV cache has strides {Tk*h*d, d, h*d}.  d_head may be any multiple of 8 in [8, 128]: the
+ *   kernels pad it to 64 or 128 with zeros on chip.  lse stays contiguous [B][h] fp32.  Same
+ *   method, kernels and results as fa_decode (bit for bit for contiguous d_head 64 / 128).
+ *   Preconditions: as fa_decode, with d_head as above; q, k, v 16-byte aligned, o 2-byte
+ *   aligned; every stride a non-negative multiple of 8 elements; k and v row strides >= d_head
+ *   with (Tk + 256) * row_stride * 2 <= FA_MAX_HEAD_BYTES; o must not overlap the inputs.
+ */
+int fa_decode_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t h, int64_t Tk, int64_t d_head,
+                      const int64_t* q_strides, const int64_t* k_strides,
+                      const int64_t* v_strides, const int64_t* o_strides, float scale,
+                      int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd / fa_bwd_f32 need: two fp32 values
@@ -248,7 +267,7 @@ int fa_gelu_bf16(const void* x, void* y, int64_t n, void* stream);
 int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t rows,
                               int64_t cols, float p, uint64_t seed, uint64_t offset, void* stream);
 
-/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_fwd_strided, fa_decode,
+/* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_fwd_strided, fa_decode(_strided),
  * fa_bwd / fa_bwd_f32, fa_bwd_strided, fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16
  * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return. */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -272,6 +291,12 @@ int fa_validate_fwd_strided(const void* q, const void* k, const void* v, const v
                             int64_t d_head, const int64_t* q_strides, const int64_t* k_strides,
                             const int64_t* v_strides, const int64_t* o_strides, int causal,
                             float scale);
+int fa_validate_decode_strided(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, int64_t B, int64_t h, int64_t Tk,
+                               int64_t d_head, const int64_t* q_strides,
+                               const int64_t* k_strides, const int64_t* v_strides,
+                               const int64_t* o_strides, float scale, int64_t num_splits,
+                               const void* workspace, size_t workspace_bytes);
 int fa_validate_decode(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, int64_t B, int64_t h, int64_t Tk, int64_t d_head,
                        float scale, int64_t num_splits, const void* workspace,

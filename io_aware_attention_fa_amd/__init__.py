@@ -17,7 +17,7 @@ from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR
                    FA_ERR_NULL, FA_ERR_PROB, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS,
                    FA_ERR_WORKSPACE, FA_OK, LIB_PATH)
 
-__all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_workspace_size", "fa_bwd",
+__all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_workspace_size", "fa_decode_strided", "fa_validate_decode_strided", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
            "fa_validate_bwd", "fa_bwd_strided", "fa_validate_bwd_strided", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
            "fa_gelu_bf16", "fa_bias_gelu_dropout_bf16", "fa_validate_gelu",
@@ -205,6 +205,68 @@ def fa_decode(q, k, v, *, num_splits: int, scale: float | None = None, o=None, l
     if st != FA_OK:
         raise FaError(st)
     return o, lse
+
+
+def _strides2(name, t):
+    """(batch, head) element strides of a 3-D [B, h, d] view with a contiguous last dim."""
+    import ctypes
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 3:
+        raise ValueError(f"{name} must be a 3-D GPU tensor [B, h, d]")
+    if t.stride(2) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return (ctypes.c_int64 * 2)(t.stride(0), t.stride(1))
+
+
+def fa_decode_strided(q, k, v, *, num_splits: int, scale: float | None = None, o=None, lse=None,
+                      workspace=None, stream=None):
+    """Split-KV decode on strided views and any head dim d <= 128 that is a multiple of 8:
+    q [B,h,d], k/v [B,h,Tk,d] bf16 views (e.g. ``cache.transpose(1, 2)`` of a [B,Tk,h,d] KV
+    cache) with a contiguous last dimension -> (o [B,h,d] bf16, lse [B,h] fp32).
+
+    ``o`` defaults to a contiguous tensor and may be any such view; ``lse`` is contiguous.
+    """
+    for name, t, nd in (("q", q, 3), ("k", k, 4), ("v", v, 4)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != nd:
+            raise ValueError(f"{name} must be a {nd}-D bf16 tensor")
+    B, h, d = q.shape
+    Tk = k.shape[2]
+    if tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o is None:
+        o = torch.empty((B, h, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, h, d):
+        raise ValueError("o must be a bf16 [B, h, d] view")
+    _check_tensor("lse", lse, torch.float32, 2)
+    need = fa_decode_workspace_size(B, h, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8, 1)
+    if len({t.device for t in (q, k, v, o, lse, workspace)}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = _lib.lib.fa_decode_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, h, Tk, d, _strides2("q", q),
+                                    _strides3("k", k), _strides3("v", v), _strides2("o", o),
+                                    scale, int(num_splits), workspace.data_ptr(),
+                                    workspace.numel(), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def fa_validate_decode_strided(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tk, d_head, q_strides,
+                               k_strides, v_strides, o_strides, scale, num_splits, ws_ptr,
+                               ws_bytes):
+    """Host-only argument check of fa_decode_strided (raw addresses; q / o strides as
+    2-sequences, k / v strides as 3-sequences, or None)."""
+    import ctypes
+    arr = [None if s_ is None else (ctypes.c_int64 * len(s_))(*s_)
+           for s_ in (q_strides, k_strides, v_strides, o_strides)]
+    return int(_lib.lib.fa_validate_decode_strided(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, h, Tk,
+                                                   d_head, *arr, float(scale), int(num_splits),
+                                                   ws_ptr, ws_bytes))
 
 
 def _bwd(entry, out_dtype, q, k, v, o, do, lse, causal, scale, dq, dk, dv, workspace, stream):

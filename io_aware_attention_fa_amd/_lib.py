@@ -31,6 +31,10 @@ SIGNATURES = {
     "fa_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64, _vp, _size,
                          _vp]),
     "fa_validate_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _f32]),
+    "fa_decode_strided": (_int, [_vp] * 5 + [_i64] * 4 + [_vp] * 4 + [_f32, _i64, _vp, _size,
+                                                                       _vp]),
+    "fa_validate_decode_strided": (_int, [_vp] * 5 + [_i64] * 4 + [_vp] * 4 + [_f32, _i64, _vp,
+                                                                                _size]),
     "fa_validate_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64,
                                   _vp, _size]),
     "fa_bwd_workspace_size": (_size, [_i64, _i64, _i64]),

@@ -42,7 +42,15 @@ struct DecodeParams {
   float* lse;
   int H, Tk, S, chunk;
   float scale_log2;
+  // general layouts (GEN variants): the true head dim d <= D (columns d .. D - 1 are zero
+  // padding on chip) and element strides: q and o (batch, head), k and v (batch, head, row)
+  int d;
+  int64_t q_b, q_h, o_b, o_h, k_b, k_h, v_b, v_h;
+  uint32_t k_t, v_t;
 };
+
+// A buffer offset beyond every head's range (heads are < 2^31 bytes): loads return zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
 
 // Merge the online-softmax state (m, l, o) of another lane / wave into this one.
 template <int N>
@@ -57,23 +65,34 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&o)[N], f
   m = mm;
 }
 
-template <int D>
+// GEN = false: contiguous tensors with d = D; GEN = true: the strides and d of DecodeParams.
+template <int D, bool GEN>
 __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;     // lanes per key row
   constexpr int KPW = 64 / LPK;  // key rows per wave-wide load
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane / LPK, c = lane % LPK;
+  const int hd = GEN ? p.d : D;                       // true head dim
+  const bool live = !GEN || 8 * c < hd;               // this lane's columns are not padding
+  const uint32_t k_t = GEN ? p.k_t : D, v_t = GEN ? p.v_t : D;
 
   const size_t bh = (size_t)b * p.H + h;
-  const size_t kbase = bh * (size_t)p.Tk * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kbase, (uint32_t)p.Tk * D * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kbase, (uint32_t)p.Tk * D * 2u);
+  const int64_t kbase = GEN ? b * p.k_b + h * p.k_h : (int64_t)bh * p.Tk * D;
+  const int64_t vbase = GEN ? b * p.v_b + h * p.v_h : (int64_t)bh * p.Tk * D;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(p.k + kbase, ((uint32_t)(p.Tk - 1) * k_t + (uint32_t)hd) * 2u);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(p.v + vbase, ((uint32_t)(p.Tk - 1) * v_t + (uint32_t)hd) * 2u);
+  // padding lanes load from past the buffers' ranges (zeros)
+  const uint32_t kcol = live ? 16u * (uint32_t)c : kPadOffset;
 
   // this lane's 8 query components, pre-multiplied by scale * log2(e)
   float qv[8];
   {
-    const u32x4_t qr = *reinterpret_cast<const u32x4_t*>(p.q + bh * D + 8 * c);
+    const int64_t qoff = GEN ? b * p.q_b + h * p.q_h : (int64_t)bh * D;
+    u32x4_t qr = u32x4_t{0u, 0u, 0u, 0u};
+    if (live) qr = *reinterpret_cast<const u32x4_t*>(p.q + qoff + 8 * c);
 #pragma unroll
     for (int e = 0; e < 8; ++e) qv[e] = bf16_elem(qr, e) * p.scale_log2;
   }
@@ -91,12 +110,12 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams 
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int key = base + u * KPW + slot;
-      kr[u] = buf_load16(rk, (uint32_t)(key * D + 8 * c) * 2u);
+      kr[u] = buf_load16(rk, (uint32_t)key * (k_t * 2u) + kcol);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int key = base + u * KPW + slot;
-      vr[u] = buf_load16(rv, (uint32_t)(key * D + 8 * c) * 2u);
+      vr[u] = buf_load16(rv, (uint32_t)key * (v_t * 2u) + kcol);
     }
     float sc[kUnroll];
 #pragma unroll
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams 
   }
 }
 
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(kThreads) void fa_decode_combine_kernel(DecodeParams p, int BH) {
   constexpr int PER = D / 64;   // output elements per lane
   const int lane = threadIdx.x & 63;
@@ -199,15 +218,21 @@ __global__ __launch_bounds__(kThreads) void fa_decode_combine_kernel(DecodeParam
     for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, os[lane + 64 * j], acc[j]);
   }
   const float inv = 1.0f / l;
+  int64_t obase = (int64_t)bh * D;
+  if (GEN) {
+    const int b = bh / p.H;
+    obase = b * p.o_b + (bh - b * p.H) * p.o_h;
+  }
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const __bf16 hv = (__bf16)(acc[j] * inv);
-    p.o[(size_t)bh * D + lane + 64 * j] = __builtin_bit_cast(uint16_t, hv);
+    if (!GEN || lane + 64 * j < p.d)
+      p.o[obase + lane + 64 * j] = __builtin_bit_cast(uint16_t, hv);
   }
   if (lane == 0) p.lse[bh] = (mstar + fast_log2(l)) * kLn2;
 }
 
-template <int D>
+template <int D, bool GEN>
 hipError_t launch(const DecodeLaunch& a, hipStream_t stream) {
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -223,24 +248,40 @@ hipError_t launch(const DecodeLaunch& a, hipStream_t stream) {
   p.S = a.num_splits;
   p.chunk = (a.Tk + a.num_splits - 1) / a.num_splits;
   p.scale_log2 = a.scale * kLog2e;
+  p.d = a.d;
+  p.q_b = a.q_s[0]; p.q_h = a.q_s[1];
+  p.o_b = a.o_s[0]; p.o_h = a.o_s[1];
+  p.k_b = a.k_s[0]; p.k_h = a.k_s[1]; p.k_t = (uint32_t)a.k_s[2];
+  p.v_b = a.v_s[0]; p.v_h = a.v_s[1]; p.v_t = (uint32_t)a.v_s[2];
   {
     void* args[] = {&p};
     const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_split_kernel<D>),
+        hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_split_kernel<D, GEN>),
                         dim3(a.num_splits, a.H, a.B), dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   int BH = a.B * a.H;
   void* args[] = {&p, &BH};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_combine_kernel<D>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_combine_kernel<D, GEN>),
                          dim3((BH + kWaves - 1) / kWaves), dim3(kThreads), args, 0, stream);
+}
+
+// GEN = false for contiguous tensors with d = D (64 or 128), else the general kernels.
+template <int D>
+hipError_t launch_d(const DecodeLaunch& a, hipStream_t stream) {
+  const int64_t H = a.H, T = a.Tk;
+  const bool dense = a.d == D && a.q_s[0] == H * D && a.q_s[1] == D && a.o_s[0] == H * D &&
+                     a.o_s[1] == D && a.k_s[2] == D && a.k_s[1] == T * D &&
+                     a.k_s[0] == H * T * D && a.v_s[2] == D && a.v_s[1] == T * D &&
+                     a.v_s[0] == H * T * D;
+  return dense ? launch<D, false>(a, stream) : launch<D, true>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.d == 64) return launch<64>(a, stream);
-  return launch<128>(a, stream);
+  if (a.d <= 64) return launch_d<64>(a, stream);
+  return launch_d<128>(a, stream);
 }
 
 }  // namespace fa

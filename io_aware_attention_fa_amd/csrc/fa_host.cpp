@@ -66,6 +66,26 @@ extern "C" int fa_fwd_strided(const void* q, const void* k, const void* v, void*
                     o_strides, causal, scale, stream, false);
 }
 
+namespace {
+int decode_launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                  int64_t h, int64_t Tk, int64_t d, const int64_t* qs, const int64_t* ks,
+                  const int64_t* vs, const int64_t* os, float scale, int64_t num_splits,
+                  void* workspace, void* stream) {
+  fa::DecodeLaunch a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.workspace = static_cast<float*>(workspace);
+  a.B = static_cast<int>(B); a.H = static_cast<int>(h); a.Tk = static_cast<int>(Tk);
+  a.d = static_cast<int>(d); a.num_splits = static_cast<int>(num_splits); a.scale = scale;
+  for (int i = 0; i < 2; ++i) {
+    a.q_s[i] = qs[i]; a.o_s[i] = os[i];
+  }
+  for (int i = 0; i < 3; ++i) {
+    a.k_s[i] = ks[i]; a.v_s[i] = vs[i];
+  }
+  return map_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
 extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
                          int64_t num_splits, void* workspace, size_t workspace_bytes,
@@ -73,12 +93,24 @@ extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, f
   const int st = fa_validate_decode(q, k, v, o, lse, B, h, Tk, d_head, scale, num_splits,
                                     workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  fa::DecodeLaunch a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.workspace = static_cast<float*>(workspace);
-  a.B = static_cast<int>(B); a.H = static_cast<int>(h); a.Tk = static_cast<int>(Tk);
-  a.d = static_cast<int>(d_head); a.num_splits = static_cast<int>(num_splits); a.scale = scale;
-  return map_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+  // contiguous q, o [B][h][d] and k, v [B][h][Tk][d]
+  const int64_t qs[2] = {h * d_head, d_head}, ks[3] = {h * Tk * d_head, Tk * d_head, d_head};
+  return decode_launch(q, k, v, o, lse, B, h, Tk, d_head, qs, ks, ks, qs, scale, num_splits,
+                       workspace, stream);
+}
+
+extern "C" int fa_decode_strided(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int64_t B, int64_t h, int64_t Tk, int64_t d_head,
+                                 const int64_t* q_strides, const int64_t* k_strides,
+                                 const int64_t* v_strides, const int64_t* o_strides, float scale,
+                                 int64_t num_splits, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  const int st = fa_validate_decode_strided(q, k, v, o, lse, B, h, Tk, d_head, q_strides,
+                                            k_strides, v_strides, o_strides, scale, num_splits,
+                                            workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  return decode_launch(q, k, v, o, lse, B, h, Tk, d_head, q_strides, k_strides, v_strides,
+                       o_strides, scale, num_splits, workspace, stream);
 }
 
 namespace {

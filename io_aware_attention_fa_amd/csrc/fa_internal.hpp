@@ -29,6 +29,8 @@ struct DecodeLaunch {
   float* workspace;
   int B, H, Tk, d, num_splits;
   float scale;
+  // element strides: q and o (batch, head), k and v (batch, head, row); last dim contiguous
+  int64_t q_s[2], o_s[2], k_s[3], v_s[3];
 };
 
 struct BwdLaunch {

@@ -81,8 +81,10 @@ extern "C" int fa_validate_fwd(const void* q, const void* k, const void* v, cons
 extern "C" size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head,
                                            int64_t num_splits) {
   if (B < 1 || h < 1 || d_head < 1 || num_splits < 1) return 0;
+  // partials are kept at the padded width (64 or 128) the kernels compute in
+  const int64_t dw = d_head <= 64 ? 64 : (d_head <= 128 ? 128 : d_head);
   return static_cast<size_t>(B) * static_cast<size_t>(h) * static_cast<size_t>(num_splits) *
-         static_cast<size_t>(d_head + 2) * sizeof(float);
+         static_cast<size_t>(dw + 2) * sizeof(float);
 }
 
 extern "C" int fa_validate_decode(const void* q, const void* k, const void* v, const void* o,
@@ -97,6 +99,44 @@ extern "C" int fa_validate_decode(const void* q, const void* k, const void* v, c
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if (num_splits < 1 || num_splits > Tk || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < fa_decode_workspace_size(B, h, d_head, num_splits))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+namespace {
+// (batch, head) strides of a one-row-per-head tensor (decode's q and o)
+bool strides2_ok(const int64_t* s, int64_t B, int64_t h) {
+  if (!s) return false;
+  const int64_t sb = s[0], sh = s[1];
+  if (sb < 0 || sh < 0 || sb % 8 != 0 || sh % 8 != 0) return false;
+  const int64_t big = INT64_MAX / 4;
+  return !((B > 1 && sb > big / (B - 1)) || (h > 1 && sh > big / (h - 1)));
+}
+}  // namespace
+
+extern "C" int fa_validate_decode_strided(const void* q, const void* k, const void* v,
+                                          const void* o, const float* lse, int64_t B, int64_t h,
+                                          int64_t Tk, int64_t d_head, const int64_t* q_strides,
+                                          const int64_t* k_strides, const int64_t* v_strides,
+                                          const int64_t* o_strides, float scale,
+                                          int64_t num_splits, const void* workspace,
+                                          size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || h < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!strides2_ok(q_strides, B, h) || !strides2_ok(o_strides, B, h)) return FA_ERR_SHAPE;
+  // the split pass reads up to 256 rows past a chunk's end (zero-filled), so one more block
+  if (!strides_ok(k_strides, Tk + 128, d_head, B, h) ||
+      !strides_ok(v_strides, Tk + 128, d_head, B, h))
+    return FA_ERR_SHAPE;
+  if (B > 65535 || h > 65535) return FA_ERR_SHAPE;   // grid y / z extents of the split pass
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (num_splits < 1 || num_splits > Tk || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 2) ||
       !aligned(lse, 4))
     return FA_ERR_ALIGN;
   if (!workspace || !aligned(workspace, 16) ||

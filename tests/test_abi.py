@@ -102,6 +102,9 @@ def test_validate_decode(fa_lib, B, h, Tk, d, S, ws_delta, code):
 def test_decode_workspace_size(fa_lib):
     assert fa_lib.fa_decode_workspace_size(64, 32, 128, 16) == 64 * 32 * 16 * 130 * 4
     assert fa_lib.fa_decode_workspace_size(0, 32, 128, 16) == 0
+    # other head dims are computed at the padded width (64 or 128)
+    assert fa_lib.fa_decode_workspace_size(2, 3, 80, 4) == 2 * 3 * 4 * 130 * 4
+    assert fa_lib.fa_decode_workspace_size(2, 3, 8, 4) == 2 * 3 * 4 * 66 * 4
     assert fa_lib.fa_validate_decode(P, P, P, P, P, 1, 1, 10, 64, 0.1, 2, 0, 10**6) == 8
     assert fa_lib.fa_validate_decode(P, P, P, P, P, 1, 1, 10, 64, 0.1, 2, P + 4, 10**6) == 8
 
@@ -284,3 +287,31 @@ def test_invalid_bwd_strided_call_touches_nothing(fa_lib):
                                  ctypes.c_void_p(ws.ctypes.data), ws.nbytes, None)
     assert st == 3
     assert np.all(out == 0x7FC1) and np.all(ws == 7)
+
+
+
+def _vds(fa_lib, **kw):
+    a = dict(B=2, h=3, Tk=500, d=80, qs=(3 * 80, 80), ks=(500 * 3 * 80, 80, 3 * 80),
+             vs=(500 * 3 * 80, 80, 3 * 80), os=(3 * 80, 80), scale=0.1, S=4, ws=P, ws_bytes=None,
+             o=P, q=P)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = fa_lib.fa_decode_workspace_size(2, 3, a["d"], 4)
+    return fa_lib.fa_validate_decode_strided(a["q"], P, P, a["o"], P, a["B"], a["h"], a["Tk"],
+                                             a["d"], a["qs"], a["ks"], a["vs"], a["os"],
+                                             a["scale"], a["S"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"d": 128, "qs": (0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 128)}, 0),
+    ({"o": P + 2}, 0),                       # o needs only 2-byte alignment
+    ({"o": 0}, 1),
+    ({"qs": None}, 2), ({"os": (3 * 80, 84)}, 2), ({"ks": (500 * 3 * 80, 80, 72)}, 2),
+    ({"vs": (0, 0, 2**25)}, 2),              # (Tk + 256) rows beyond 2^31 bytes
+    ({"d": 100}, 3), ({"d": 136}, 3),
+    ({"q": P + 8}, 5), ({"o": P + 1}, 5),
+    ({"scale": math.inf}, 6), ({"S": 0}, 7), ({"S": 501}, 7), ({"ws_bytes": 64}, 8),
+])
+def test_validate_decode_strided(fa_lib, kw, code):
+    assert _vds(fa_lib, **kw) == code
