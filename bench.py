@@ -237,10 +237,11 @@ def measure_softmax(args, fa, si, torch):
     return res
 
 
-def measure_layouts(args, fa, si, cm, torch):
+def measure_layouts(args, fa, si, cm, torch, dec=None):
     """The forward and the backward on layout variants: the prefill workload with the tensors in
     [B][T][h][d] (strided views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the pages'
-    padding example."""
+    padding example; with ``dec`` = (workload, q, k, v) of the decode, also the decode on the same
+    KV cache stored as [B][Tk][h][d]."""
     import numpy as np
     peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
     K = args.extra_steps or 20
@@ -312,6 +313,31 @@ def measure_layouts(args, fa, si, cm, torch):
                                "layout": "BTHD strided" if strided else "BHTD contiguous",
                                "flops": flops}}
         del tq, tk, tv, tdo, to, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    if dec is not None:
+        wd, dq_, dk_, dv_ = dec
+        kc = dk_.transpose(1, 2).contiguous().transpose(1, 2)   # [B][Tk][h][d] storage
+        vc = dv_.transpose(1, 2).contiguous().transpose(1, 2)
+        o = torch.empty_like(dq_)
+        lse = torch.empty((wd.B, wd.h), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_decode_workspace_size(wd.B, wd.h, wd.d, wd.num_splits),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: fa.fa_decode_strided(dq_, kc, vc, num_splits=wd.num_splits, scale=wd.scale,
+                                            o=o, lse=lse, workspace=ws)
+        ms = time_calls(torch, call, 3, K)
+        kv = wd.B * wd.h * wd.Tk * cm.decode_kv_bytes_per_token(wd.d)
+        gbs = kv / (ms * 1e-3) / 1e9
+        hbm = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
+        eprint(f"[bench] layout decode_bthd: B={wd.B} h={wd.h} Tk={wd.Tk} d={wd.d} "
+               f"S={wd.num_splits} avg {ms:.4f} ms  {gbs:.0f} GB/s  {100 * gbs / hbm:.1f}%")
+        res["decode_bthd"] = {
+            "metric": "decode HBM GB/s (K+V bytes / split+combine time), KV cache in [B][Tk][h][d]",
+            "value": gbs, "unit": "GB/s", "steps": K, "warmup": 3, "avg_ms": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": hbm, "unit": "GB/s",
+                         "frac": gbs / hbm, "traffic": None},
+            "config": {"B": wd.B, "h": wd.h, "Tk": wd.Tk, "d_head": wd.d,
+                       "num_splits": wd.num_splits, "layout": "BTHD strided KV cache"}}
+        del kc, vc, o, lse, ws
         torch.cuda.empty_cache()
     return res
 
@@ -594,7 +620,8 @@ def main():
     if do_elementwise:
         out.update(measure_elementwise(args, fa, si, torch))
     if do_layouts:
-        out["layouts"] = measure_layouts(args, fa, si, cm, torch)
+        out["layouts"] = measure_layouts(args, fa, si, cm, torch,
+                                         dec=(wd, dq, dk, dv) if do_decode else None)
     print(json.dumps(out), flush=True)
 
 
