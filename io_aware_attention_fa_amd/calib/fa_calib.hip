@@ -2,6 +2,8 @@
 //   mfma   : dense bf16 v_mfma_f32_32x32x16_bf16 throughput (8 independent accumulators / wave)
 //   exp    : v_exp_f32 throughput (16 independent chains / lane, x <- 2^-x stays in [0.5, 1])
 //   lds    : ds_read_b128 and ds_read_b64_tr_b16 bandwidth (conflict-free addresses)
+//   ldsmfma: MFMAs whose A operands stream from LDS (random bf16 data), with or without
+//            operand reuse and a share of fma/exp vector work, at two waves per SIMD
 //   hbm    : streaming read of a large buffer with 16-byte buffer loads
 //   clock  : shader clock from s_memtime against the 100 MHz s_memrealtime counter
 // Every kernel reads and writes only inside the buffers it is given.
@@ -164,6 +166,103 @@ __global__ __launch_bounds__(256) void k_lds_tr(uint32_t* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// MFMA fed from LDS, the prefill forward's operand mix: 128 KB of random bf16 in LDS (one
+// workgroup per CU), every A operand a row read (ds_read_b128) or a transposing read (two
+// ds_read_b64_tr_b16), alternately, through an 8-deep register ring; B operands in registers.
+// REUSE = 1: each A operand feeds one MFMA (a wave owning 32 query rows); REUSE = 2: two MFMAs
+// with two B operands (a wave owning 64).  NV vector instructions per 16 MFMAs, 16 of them
+// v_exp_f32 when NV > 0, the rest v_fma_f32.  All LDS addresses stay inside the 128 KB array.
+template <int REUSE, int NV>
+__global__ __launch_bounds__(512) void k_lds_mfma(float* out, int iters) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sm[65536];
+  for (int i = threadIdx.x; i < 65536; i += blockDim.x) {
+    uint32_t h = (uint32_t)i * 2654435761u + blockIdx.x * 40503u;
+    h ^= h >> 15;
+    h *= 2246822519u;
+    h ^= h >> 13;
+    sm[i] = (uint16_t)(0x3f00u | (h & 0x807fu));   // +-[0.5, 1) with random mantissas
+  }
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(sm);
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  // row reads: 256-byte rows, chunk XOR-swizzled by row (conflict-free); at most 57.6 KB + 8 KB
+  uint32_t ra = base + (w & 3) * 16384u + r32 * 256u + 16u * (g ^ (r32 & 15));
+  // transposing reads: 16-lane groups read 4 rows x 16 bytes; at most 82 KB
+  const uint32_t x = (lane & 15) >> 2, dh = (lane >> 4) & 1, r = 4 * g + x;
+  uint32_t ta = base + (w & 3) * 16384u + r * 256u +
+                16u * ((2 * dh + ((lane & 3) >> 1)) ^ (4 * (r & 3))) + 8u * (lane & 1);
+  asm volatile("" : "+v"(ra), "+v"(ta));
+  constexpr int NACC = REUSE == 1 ? 4 : 8, NA = 16 / REUSE, RING = 8;
+  f32x16_t acc[NACC];
+  for (int i = 0; i < NACC; ++i) acc[i] = f32x16_t{};
+  bf16x8_t b[2];
+  for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 8; ++i) {
+      uint32_t h = (threadIdx.x * 16u + 8u * j + i) * 2654435761u;
+      h ^= h >> 15;
+      h *= 2246822519u;
+      h ^= h >> 13;
+      b[j][i] = __builtin_bit_cast(__bf16, (uint16_t)(0x3f00u | (h & 0x807fu)));
+    }
+  float xv[16];
+  for (int i = 0; i < 16; ++i) xv[i] = 0.5f + 0.01f * i + 1e-6f * threadIdx.x;
+  auto rd = [&](int i) -> bf16x8_t {
+    typedef __attribute__((address_space(3))) s16x4_t* lp;
+    if (i & 1) {
+      const uint32_t a0 = ta + (uint32_t)((i >> 1) & 7) * 4096u + 64u * ((i >> 4) & 3);
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(uintptr_t)a0);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(uintptr_t)(a0 + 2048));
+      const u32x4_t v = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+    const uint32_t a0 = (ra ^ (32u * ((i >> 1) & 7))) + 8192u * ((i >> 4) & 1);
+    return *(__attribute__((address_space(3))) const bf16x8_t*)(uintptr_t)a0;
+  };
+  bf16x8_t ring[RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i) ring[i] = rd(i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const bf16x8_t av = ring[a % RING];
+      ring[a % RING] = rd(a + RING);
+#pragma unroll
+      for (int u = 0; u < REUSE; ++u) {
+        const int m = a * REUSE + u;
+        acc[m % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[u], acc[m % NACC], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if (v < 16)
+        xv[v & 15] = __builtin_amdgcn_exp2f(xv[v & 15]);
+      else
+        xv[v & 15] = __builtin_fmaf(xv[v & 15], 1.0000001f, -0.0000001f);
+    }
+    // per A operand: its MFMAs, each followed by NV / 16 vector instructions, then its reads
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int u = 0; u < REUSE; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (NV) __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, NV / 16, 0);
+      }
+      if (a & 1)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += xv[i] + acc[i % NACC][i];
+  for (int i = 0; i < RING; ++i) s += (float)ring[i][i & 7];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // Streaming read: thread t reads 16-byte chunks t, t + stride, ... of n16 chunks.
 __global__ __launch_bounds__(256) void k_hbm_read(const u32x4_t* __restrict__ src, long n16,
                                                   uint32_t* out) {
@@ -233,6 +332,18 @@ int calib_lds_b128(uint32_t* out, int blocks, int iters, void* s) {
 int calib_lds_tr(uint32_t* out, int blocks, int iters, void* s) {
   hipLaunchKernelGGL(k_lds_tr, dim3(blocks), dim3(256), 0, (hipStream_t)s, out, iters);
   return (int)hipGetLastError();
+}
+int calib_lds_mfma(float* out, int blocks, int iters, int reuse, int nv, void* s) {
+  const hipStream_t st = (hipStream_t)s;
+#define FA_CALIB_LM(R, N)                                                                  \
+  if (reuse == R && nv == N) {                                                             \
+    hipLaunchKernelGGL((k_lds_mfma<R, N>), dim3(blocks), dim3(512), 0, st, out, iters);   \
+    return (int)hipGetLastError();                                                         \
+  }
+  FA_CALIB_LM(1, 0) FA_CALIB_LM(2, 0) FA_CALIB_LM(1, 48) FA_CALIB_LM(2, 48) FA_CALIB_LM(1, 80)
+  FA_CALIB_LM(2, 80)
+#undef FA_CALIB_LM
+  return (int)hipErrorInvalidValue;
 }
 int calib_hbm_read(const void* src, long n16, uint32_t* out, int blocks, void* s) {
   hipLaunchKernelGGL(k_hbm_read, dim3(blocks), dim3(256), 0, (hipStream_t)s,

@@ -1,8 +1,9 @@
 """Run the gfx950 calibration microbenchmarks (libfa_calib.so) and print one JSON object.
 
 Measures the ceilings the attention kernels are held against: dense bf16 MFMA FLOP/s, v_exp_f32
-rate, LDS read bandwidth (ds_read_b128 and ds_read_b64_tr_b16), streaming HBM read bandwidth and
-the shader clock.  Usage: python -m io_aware_attention_fa_amd.calibrate
+rate, LDS read bandwidth (ds_read_b128 and ds_read_b64_tr_b16), MFMAs fed from LDS with random
+data, streaming HBM read bandwidth and the shader clock.
+Usage: python -m io_aware_attention_fa_amd.calibrate
 """
 from __future__ import annotations
 
@@ -82,6 +83,16 @@ def main():
     bps = blocks_l * 256 * iters * 8 * 8 / t
     res["lds_tr16_b64_bytes_per_s"] = bps
     res["lds_tr16_b64_bytes_per_clk_per_cu_at_2400"] = bps / cus / 2.4e9
+
+    # MFMAs fed from LDS with random data (two waves per SIMD, one workgroup per CU): with and
+    # without reuse of each A operand, and with 0, 48 or 80 vector instructions per 16 MFMAs
+    iters = 4000
+    for reuse in (1, 2):
+        for nv in (0, 48, 80):
+            t = _time(lambda: lib.calib_lds_mfma(ctypes.c_void_p(out.data_ptr()), cus, iters,
+                                                 reuse, nv, st))
+            flops = cus * 8 * iters * 16 * 32768
+            res[f"lds_mfma_random_tflops_reuse{reuse}_valu{nv}"] = flops / t / 1e12
 
     n = 4 << 30
     src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
