@@ -152,6 +152,27 @@ def test_persistent_schedule_shapes(gpu, B, h, Tq, Tk, d, causal):
     assert torch.isfinite(res["o32"]).all()
 
 
+@pytest.mark.parametrize("d,causal", [(64, True), (64, False), (128, True)])
+def test_key_spikes_raise_the_running_max(gpu, d, causal):
+    """1% of the keys scaled x8 (the long-context recipe) at a size the oracle runs whole:
+    the running max jumps many times per row, so the rescale path runs often."""
+    wl = si.custom_workload(2, 3, 1500, 1500, d, causal, key_spike_frac=0.01,
+                            key_spike_mult=8.0)
+    q, k, v = si.make_inputs(wl, seed=23, threads=4)
+    res = run_fwd(gpu, q, k, v, causal, wl.scale)
+    o32 = res["o32"].cpu().numpy()
+    l32 = res["lse32"].cpu().numpy()
+    for bh in [(0, 0), (1, 2)]:
+        o_ref, l_ref = ref.naive_attention_head(si.bf16_bits_to_f64(q[bh]),
+                                                si.bf16_bits_to_f64(k[bh]),
+                                                si.bf16_bits_to_f64(v[bh]), wl.scale, causal)
+        d_o = float(np.max(np.abs(o32[bh] - o_ref)))
+        d_l = float(np.max(np.abs(l32[bh] - l_ref)))
+        log(f"[parity] keyspikes d={d} causal={causal} head {bh}: max|dO|={d_o:.3e} "
+            f"max|dLSE|={d_l:.3e}")
+        assert d_o <= O_TOL and d_l <= LSE_TOL
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_row_zero_is_exactly_first_value_row(gpu, d):
     wl = si.custom_workload(2, 4, 300, 300, d, True)
@@ -164,11 +185,12 @@ def test_causal_row_zero_is_exactly_first_value_row(gpu, d):
     assert np.max(np.abs(res["lse32"].cpu().numpy()[:, :, 0] - lse0)) <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal,Tq,Tk", [(True, 300, 300), (True, 100, 357), (False, 130, 257)])
-def test_zero_queries_give_log_count_and_mean(gpu, causal, Tq, Tk):
-    wl = si.custom_workload(1, 2, Tq, Tk, 128, causal)
+def test_zero_queries_give_log_count_and_mean(gpu, causal, Tq, Tk, d):
+    wl = si.custom_workload(1, 2, Tq, Tk, d, causal)
     _, k, v = si.make_inputs(wl, seed=9, threads=2)
-    q = np.zeros((1, 2, Tq, 128), dtype=np.uint16)
+    q = np.zeros((1, 2, Tq, d), dtype=np.uint16)
     res = run_fwd(gpu, q, k, v, causal, wl.scale)
     counts = np.arange(Tq) + (Tk - Tq) + 1 if causal else np.full(Tq, Tk)
     lse = res["lse32"].cpu().numpy()
@@ -191,9 +213,10 @@ def test_constant_values_give_that_constant(gpu):
     assert np.all(err[:, :, 0] == 0.0)   # row 0 sees one key: p = 1 exactly
 
 
-def test_large_scores_stay_finite_and_exact(gpu):
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_scores_stay_finite_and_exact(gpu, d):
     """Scores in the hundreds: exp overflows unless the running max is subtracted."""
-    wl = si.custom_workload(1, 2, 256, 256, 128, True)
+    wl = si.custom_workload(1, 2, 256, 256, d, True)
     q, k, v = si.make_inputs(wl, seed=14, threads=2)
     scale = 12.0
     res = run_fwd(gpu, q, k, v, True, scale)
