@@ -47,8 +47,8 @@ enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,             /* a required pointer is NULL                                    */
   FA_ERR_SHAPE = 2,            /* a size is < 1, or too large for the kernels' 32-bit offsets   */
-  FA_ERR_HEAD_DIM = 3,         /* d_head not supported (forward: multiple of 8 in [8, 128];     */
-                               /* decode and backward: 64 or 128)                               */
+  FA_ERR_HEAD_DIM = 3,         /* d_head not a multiple of 8 in [8, 128] (fa_bwd_f32: not 64 or */
+                               /* 128)                                                          */
   FA_ERR_CAUSAL_TQ_GT_TK = 4,  /* causal with Tq > Tk (a query row would see no key)            */
   FA_ERR_ALIGN = 5,            /* a tensor pointer is not 16-byte aligned (LSE: 4-byte)          */
   FA_ERR_SCALE = 6,            /* scale is not finite, or causal is not 0 / 1                   */
@@ -127,7 +127,8 @@ size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t nu
  *   `workspace`, a second pass rescales the chunks onto their common max and normalises
  *   (page "Fusion and IO-aware kernels", "Where it breaks": decode is KV-cache bound and is split
  *   across the sequence; the merge is the rescale of the online-softmax recurrence).
- *   The result does not depend on num_splits beyond rounding.
+ *   The result does not depend on num_splits beyond rounding.  d_head as fa_fwd (any multiple
+ *   of 8 in [8, 128], padded to 64 or 128 with zeros on chip).
  *   Preconditions: as fa_fwd for pointers and sizes; 1 <= num_splits <= min(Tk, FA_MAX_SPLITS);
  *   workspace 16-byte aligned with workspace_bytes >= fa_decode_workspace_size(B, h, d_head,
  *   num_splits).  The workspace holds no state between calls.
@@ -175,6 +176,7 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq);
  *   Precision: bf16 inputs, fp32 accumulation; P and dS are rounded to bf16 (round to nearest
  *   even) as operands of the gradient products; outputs rounded to bf16.  The result is
  *   deterministic (no atomics): the same inputs give the same bits.
+ *   d_head as fa_fwd (any multiple of 8 in [8, 128], padded to 64 or 128 with zeros on chip).
  *   Preconditions: as fa_fwd for sizes and alignment (all tensors 16-byte aligned, lse 4-byte);
  *   workspace 16-byte aligned with workspace_bytes >= fa_bwd_workspace_size(B, h, Tq); the
  *   outputs and the workspace must not overlap the inputs or each other.  Every element of dq,
@@ -188,6 +190,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /*
  * fa_bwd_f32 -- the same computation and kernels with dq, dk, dv stored in fp32 (parity
  *   diagnostics: fa_bwd's outputs are the round-to-nearest-even of these, bit for bit).
+ *   d_head must be 64 or 128 (FA_ERR_HEAD_DIM otherwise); everything else as fa_bwd.
  */
 int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, float* dq, float* dk, float* dv,
@@ -269,7 +272,8 @@ int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t 
 
 /* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_fwd_strided, fa_decode(_strided),
  * fa_bwd / fa_bwd_f32, fa_bwd_strided, fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16
- * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return. */
+ * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return
+ * (fa_validate_bwd checks fa_bwd's rules; fa_bwd_f32 also needs d_head 64 or 128). */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, const void* dq, const void* dk,
                     const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,

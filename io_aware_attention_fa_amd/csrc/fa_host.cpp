@@ -142,6 +142,8 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   const int st = fa_validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, h, Tq, Tk, d, causal, scale,
                                  workspace, workspace_bytes);
   if (st != FA_OK) return st;
+  // the fp32-output kernels exist for the unpadded head dims only
+  if (out_f32 && d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   // contiguous [B][h][T][d]
   const int64_t qs[3] = {h * Tq * d, Tq * d, d}, ks[3] = {h * Tk * d, Tk * d, d};
   const int64_t* const s[8] = {qs, ks, ks, qs, qs, qs, ks, ks};

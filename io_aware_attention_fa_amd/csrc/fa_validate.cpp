@@ -10,10 +10,8 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool head_dim_ok(int64_t d) { return d == 64 || d == 128; }
-
-// The forward pads any multiple of 8 up to 128 on chip (16-byte chunks of 8 bf16).
-bool fwd_head_dim_ok(int64_t d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+// The kernels pad any multiple of 8 up to 128 on chip (16-byte chunks of 8 bf16) to 64 or 128.
+bool head_dim_ok(int64_t d) { return d >= 8 && d <= 128 && d % 8 == 0; }
 
 // Strided head: rows of stride t (>= d, a multiple of 8 elements so that rows stay 16-byte
 // aligned), the head's bytes including one 128-row block of reads past the end below 2^31.
@@ -44,7 +42,7 @@ extern "C" int fa_validate_fwd_strided(const void* q, const void* k, const void*
                                        int causal, float scale) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
-  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!strides_ok(q_strides, Tq, d_head, B, h) || !strides_ok(k_strides, Tk, d_head, B, h) ||
       !strides_ok(v_strides, Tk, d_head, B, h) || !strides_ok(o_strides, Tq, d_head, B, h))
     return FA_ERR_SHAPE;
@@ -64,7 +62,7 @@ extern "C" int fa_validate_fwd(const void* q, const void* k, const void* v, cons
                                int64_t d_head, int causal, float scale) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
-  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!head_bytes_ok(Tq, d_head) || !head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
   // the grid is one workgroup per (128-row query block, head, batch) and must fit in 31 bits
   const int64_t nqb = (Tq + 127) / 128;
@@ -127,7 +125,7 @@ extern "C" int fa_validate_decode_strided(const void* q, const void* k, const vo
                                           size_t workspace_bytes) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || h < 1 || Tk < 1) return FA_ERR_SHAPE;
-  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!strides2_ok(q_strides, B, h) || !strides2_ok(o_strides, B, h)) return FA_ERR_SHAPE;
   // the split pass reads up to 256 rows past a chunk's end (zero-filled), so one more block
   if (!strides_ok(k_strides, Tk + 128, d_head, B, h) ||
@@ -191,7 +189,7 @@ extern "C" int fa_validate_bwd_strided(
     float scale, const void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
-  if (!fwd_head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!strides_ok(q_strides, Tq, d_head, B, h) || !strides_ok(o_strides, Tq, d_head, B, h) ||
       !strides_ok(do_strides, Tq, d_head, B, h) || !strides_ok(dq_strides, Tq, d_head, B, h) ||
       !strides_ok(k_strides, Tk, d_head, B, h) || !strides_ok(v_strides, Tk, d_head, B, h) ||

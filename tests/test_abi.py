@@ -91,7 +91,10 @@ def test_validate_fwd(fa_lib, args, code):
     (2, 3, 300, 128, 257, 0, 7),
     (2, 3, 100, 128, 100, 0, 0),
     (2, 3, 100, 128, 4, -4, 8),
-    (2, 3, 100, 80, 4, 0, 3),
+    (2, 3, 100, 80, 4, 0, 0),      # padded head dims run the padded kernels
+    (2, 3, 100, 8, 4, 0, 0),
+    (2, 3, 100, 84, 4, 0, 3),      # not a multiple of 8
+    (2, 3, 100, 136, 4, 0, 3),     # above 128
     (0, 3, 100, 128, 4, 0, 2),
 ])
 def test_validate_decode(fa_lib, B, h, Tk, d, S, ws_delta, code):
@@ -153,7 +156,7 @@ def _vb(fa_lib, **kw):
     ({}, 0),
     ({"do": 0}, 1), ({"dv": 0}, 1), ({"lse": 0}, 1),
     ({"Tq": 0}, 2), ({"B": 0}, 2), ({"Tk": 2**30}, 2),
-    ({"d": 80}, 3),
+    ({"d": 80}, 0), ({"d": 8}, 0), ({"d": 84}, 3), ({"d": 0}, 3), ({"d": 136}, 3),
     ({"Tq": 121}, 4), ({"Tq": 121, "causal": 0}, 0),
     ({"do": P + 8}, 5), ({"dk": P + 2}, 5), ({"lse": P + 2}, 5),
     ({"scale": math.nan}, 6), ({"causal": 3}, 6),
@@ -170,8 +173,12 @@ def test_invalid_bwd_call_touches_nothing(fa_lib):
     lse = np.zeros(64, dtype=np.float32)
     ws = np.full(4096, 7, dtype=np.uint8)
     a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, buf, buf, lse, out, out, out)]
-    st = _lib.lib.fa_bwd(*a, 1, 1, 16, 16, 96, 0, 0.125, ctypes.c_void_p(ws.ctypes.data),
+    st = _lib.lib.fa_bwd(*a, 1, 1, 16, 16, 100, 0, 0.125, ctypes.c_void_p(ws.ctypes.data),
                          ws.nbytes, None)
+    assert st == 3
+    # fp32 outputs: unpadded head dims only
+    st = _lib.lib.fa_bwd_f32(*a, 1, 1, 16, 16, 96, 0, 0.125, ctypes.c_void_p(ws.ctypes.data),
+                             ws.nbytes, None)
     assert st == 3
     st = _lib.lib.fa_bwd_f32(*a, 1, 1, 17, 16, 64, 1, 0.125, ctypes.c_void_p(ws.ctypes.data),
                              ws.nbytes, None)

@@ -76,7 +76,11 @@ def test_decode_padded_head_dims(gpu, d):
     wl, q, k, v = _case(B, h, Tk, d, seed=32)
     o, lse = gpu.fa_decode_strided(to_gpu(q), to_gpu(k), to_gpu(v), num_splits=5,
                                    scale=wl.scale)
+    # the contiguous entry point takes the same padded kernels for the same tensors
+    o2, lse2 = gpu.fa_decode(to_gpu(q), to_gpu(k), to_gpu(v), num_splits=5, scale=wl.scale)
     torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(lse2, lse), \
+        f"{tag}: fa_decode differs from fa_decode_strided"
     _oracle_gate(tag, o, lse, q, k, v, wl.scale)
 
 
