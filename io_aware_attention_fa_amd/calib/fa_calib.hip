@@ -5,6 +5,7 @@
 //   ldsmfma: MFMAs whose A operands stream from LDS (random bf16 data), with or without
 //            operand reuse and a share of fma/exp vector work, at two waves per SIMD
 //   hbm    : streaming read of a large buffer with 16-byte buffer loads
+//   atomic : fp32 atomic adds (no return value) into an L2-sized or an HBM-sized buffer
 //   clock  : shader clock from s_memtime against the 100 MHz s_memrealtime counter
 // Every kernel reads and writes only inside the buffers it is given.
 #include <hip/hip_runtime.h>
@@ -280,6 +281,19 @@ __global__ __launch_bounds__(256) void k_hbm_read(const u32x4_t* __restrict__ sr
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// fp32 atomic adds without a return value (global_atomic_add_f32): each wave adds to one
+// 256-byte run of 64 floats per iteration; consecutive iterations of a wave move by a large odd
+// stride, so the runs spread over the buffer.  n_mask = (floats in the buffer) - 1, a power of
+// two minus one: every index stays inside the buffer.
+__global__ __launch_bounds__(256) void k_atomic_add(float* buf, uint32_t n_mask, int iters) {
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, lane = threadIdx.x & 63;
+  uint32_t run = wave * 2654435761u;
+  for (int it = 0; it < iters; ++it) {
+    unsafeAtomicAdd(buf + (((run & ~63u) + lane) & n_mask), 1.0f);
+    run += 40503u * 64u + 64u;
+  }
+}
+
 __global__ void k_clock(unsigned long long* out, int spin) {
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
@@ -348,6 +362,11 @@ int calib_lds_mfma(float* out, int blocks, int iters, int reuse, int nv, void* s
 int calib_hbm_read(const void* src, long n16, uint32_t* out, int blocks, void* s) {
   hipLaunchKernelGGL(k_hbm_read, dim3(blocks), dim3(256), 0, (hipStream_t)s,
                      (const u32x4_t*)src, n16, out);
+  return (int)hipGetLastError();
+}
+int calib_atomic_add(float* buf, unsigned int n_mask, int blocks, int iters, void* s) {
+  hipLaunchKernelGGL(k_atomic_add, dim3(blocks), dim3(256), 0, (hipStream_t)s, buf, n_mask,
+                     iters);
   return (int)hipGetLastError();
 }
 int calib_clock(unsigned long long* out, int spin, void* s) {

@@ -2,7 +2,7 @@
 
 Measures the ceilings the attention kernels are held against: dense bf16 MFMA FLOP/s, v_exp_f32
 rate, LDS read bandwidth (ds_read_b128 and ds_read_b64_tr_b16), MFMAs fed from LDS with random
-data, streaming HBM read bandwidth and the shader clock.
+data, fp32 atomic-add throughput, streaming HBM read bandwidth and the shader clock.
 Usage: python -m io_aware_attention_fa_amd.calibrate
 """
 from __future__ import annotations
@@ -93,6 +93,17 @@ def main():
                                                  reuse, nv, st))
             flops = cus * 8 * iters * 16 * 32768
             res[f"lds_mfma_random_tflops_reuse{reuse}_valu{nv}"] = flops / t / 1e12
+
+    # fp32 atomic adds without a return value, 256-byte runs per wave: payload bytes per second
+    # into a 4 MiB (L2-sized) and a 512 MiB buffer
+    for mib in (4, 512):
+        nf = mib << 18   # floats
+        acc = torch.zeros(nf, dtype=torch.float32, device="cuda")
+        blocks_a, iters_a = cus * 8, 2000
+        t = _time(lambda: lib.calib_atomic_add(ctypes.c_void_p(acc.data_ptr()), nf - 1, blocks_a,
+                                               iters_a, st))
+        res[f"atomic_add_f32_GBps_{mib}MiB"] = blocks_a * 256 * iters_a * 4 / t / 1e9
+        del acc
 
     n = 4 << 30
     src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
