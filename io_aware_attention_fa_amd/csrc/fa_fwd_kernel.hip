@@ -143,7 +143,7 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) 
 // Matrix sections (see the kernel): scores only (first tile of a block), both products, or the
 // P^T product only (after the last tile).
 constexpr int kSecScores = 0, kSecBoth = 1, kSecValues = 2;
-constexpr int kRing = 8;   // operand registers in flight per matrix section
+constexpr int kRing = 4;   // operand registers in flight per matrix section
 
 // Operand order of a matrix section: scores only = the NK K operands; both = VH V^T operands,
 // the NK K operands, the other NV - VH V^T operands; values only = the NV V^T operands.  kPre
