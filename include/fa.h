@@ -103,7 +103,9 @@ int fa_fwd_o32(const void* q, const void* k, const void* v, float* o, float* lse
  *   contiguous [B][h][Tq] fp32; o is bf16.  Same computation, kernel and results as fa_fwd.
  *   Preconditions: as fa_fwd, and for each tensor: row stride >= d_head, every stride a
  *   non-negative multiple of 8 elements (rows stay 16-byte aligned), and
- *   (T + 128) * row_stride * 2 <= FA_MAX_HEAD_BYTES.  o must not overlap q, k, v or lse.
+ *   (T + 128) * row_stride * 2 <= FA_MAX_HEAD_BYTES.  o must not overlap q, k, v or lse, and
+ *   its strides must not make it overlap itself (FA_ERR_SHAPE otherwise; q, k, v may broadcast
+ *   with stride 0).
  */
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t B, int64_t h, int64_t Tq, int64_t Tk, int64_t d_head,
@@ -112,7 +114,9 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, float scale, void* stream);
 
 /*
- * fa_decode_workspace_size -- bytes of device workspace fa_decode / fa_decode_strided need:
+ * fa_decode_workspace_size -- bytes of device workspace fa_decode / fa_decode_strided need
+ *   (the caller allocates it, as the host wrapper of page "Chapter 10 Writing and Benchmarking
+ *   Custom Kernels", section 10.2.1, allocates the kernel's output before launching it):
  *   B * h * num_splits * (w + 2) fp32 partials (chunk max, denominator, w outputs), where w is
  *   the width the kernels compute in: 64 for d_head <= 64, 128 for d_head <= 128 (d_head
  *   itself when larger).  Returns 0 for sizes < 1.
@@ -147,7 +151,8 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
  *   method, kernels and results as fa_decode (bit for bit for contiguous d_head 64 / 128).
  *   Preconditions: as fa_decode, with d_head as above; q, k, v 16-byte aligned, o 2-byte
  *   aligned; every stride a non-negative multiple of 8 elements; k and v row strides >= d_head
- *   with (Tk + 256) * row_stride * 2 <= FA_MAX_HEAD_BYTES; o must not overlap the inputs.
+ *   with (Tk + 256) * row_stride * 2 <= FA_MAX_HEAD_BYTES; o must not overlap the inputs, and
+ *   its strides must not make it overlap itself (FA_ERR_SHAPE otherwise).
  */
 int fa_decode_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t B, int64_t h, int64_t Tk, int64_t d_head,
@@ -209,7 +214,8 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
  *   Preconditions: as fa_bwd, with d_head as above, and for each tensor: row stride >= d_head,
  *   every stride a non-negative multiple of 8 elements, and
  *   (T + 128) * row_stride * 2 <= FA_MAX_HEAD_BYTES (T = Tq for q, o, dout, dq; Tk for k, v,
- *   dk, dv).  The outputs must not overlap the inputs, the workspace or each other.
+ *   dk, dv).  The outputs must not overlap the inputs, the workspace or each other, and the
+ *   strides of dq, dk and dv must not make one overlap itself (FA_ERR_SHAPE otherwise).
  */
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv,
@@ -273,7 +279,13 @@ int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* y, int64_t 
 /* Host-only argument checks used by fa_fwd / fa_fwd_o32, fa_fwd_strided, fa_decode(_strided),
  * fa_bwd / fa_bwd_f32, fa_bwd_strided, fa_softmax_rows, fa_gelu_* and fa_bias_gelu_dropout_bf16
  * (no HIP call is made).  Return FA_OK or the FA_ERR_* code the entry point would return
- * (fa_validate_bwd checks fa_bwd's rules; fa_bwd_f32 also needs d_head 64 or 128). */
+ * (fa_validate_bwd checks fa_bwd's rules; fa_bwd_f32 also needs d_head 64 or 128).
+ * They are the checking half of the host wrapper of page "Chapter 10 Writing and Benchmarking
+ * Custom Kernels", section 10.2.1 (check the inputs, allocate the output, size the grid by
+ * ceiling division, launch), returning a status code where that wrapper raises; the strided
+ * checks also reject an output whose strides make it overlap itself (a stride of 0 or one
+ * inside the span of a smaller one), which inputs may do (e.g. one K/V head broadcast to
+ * several query heads). */
 int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, const void* dq, const void* dk,
                     const void* dv, int64_t B, int64_t h, int64_t Tq, int64_t Tk,
@@ -311,10 +323,13 @@ int fa_validate_gelu(const void* x, const void* y, int64_t n);
 int fa_validate_bias_gelu_dropout(const void* x, const void* bias, const void* y, int64_t rows,
                                   int64_t cols, float p);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL): the message of the failed
+ * check, which the wrapper of page "Chapter 10 Writing and Benchmarking Custom Kernels", section
+ * 10.2.1 raises as an exception and the Python binding raises from this string. */
 const char* fa_status_str(int status);
 
-/* The hipError_t behind this thread's last FA_ERR_HIP (0 if none). */
+/* The hipError_t behind this thread's last FA_ERR_HIP (0 if none): the launch-error check that
+ * follows the kernel launch in that wrapper. */
 int fa_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -51,6 +51,7 @@
 
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+#include "fa_lds.hpp"
 
 namespace fa {
 namespace {
@@ -62,9 +63,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;     // LDS ring depth
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8),
-// waiting on vector-memory operations only.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kVmcnt0 = vmcnt_imm(0);
 
 struct FwdParams {
@@ -119,27 +117,6 @@ constexpr int kVmcntQ = vmcnt_imm(D / 16);
 template <int D>
 constexpr int kVmcntQTile = vmcnt_imm(D / 16 + 2 * Tile<D>::LOADS_PER_WAVE);
 
-// One buffer_load_dwordx4 ... lds: lane l reads 16 bytes at byte offset voff of the buffer
-// (zeros past its end) and writes them to LDS bytes [m0 + 16*l, m0 + 16*l + 16).  Written as
-// inline assembly so that the compiler neither tracks it (it would otherwise wait for the load
-// before any later LDS read it cannot prove disjoint) nor moves LDS accesses across it; the
-// kernel waits for these loads itself with s_waitcnt vmcnt.
-__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t m0, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(m0), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
-// Buffer resource words for lds_dma16: base, stride 0, byte range, raw 32-bit dword format.
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
 // Matrix sections (see the kernel): scores only (first tile of a block), both products, or the
 // P^T product only (after the last tile).
 constexpr int kSecScores = 0, kSecBoth = 1, kSecValues = 2;
@@ -178,15 +155,6 @@ __device__ __forceinline__ void sched_refills() {
   }
 }
 
-// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j receives,
-// for t = 0..3, the 16-bit element j % 4 of the 8 bytes addressed by lane 4t + j / 4.
-__device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
-  typedef short s16x4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4_t* lds_ptr_t;
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(uintptr_t)addr);
-  return __builtin_bit_cast(u32x2_t, v);
-}
-
 // 16- and 8-byte LDS accesses at a byte address.
 __device__ __forceinline__ u32x4_t lds_read16u(uint32_t addr) {
   typedef __attribute__((address_space(3))) const u32x4_t* lds_ptr_t;
@@ -195,12 +163,6 @@ __device__ __forceinline__ u32x4_t lds_read16u(uint32_t addr) {
 __device__ __forceinline__ void lds_write8(uint32_t addr, u32x2_t v) {
   typedef __attribute__((address_space(3))) u32x2_t* lds_ptr_t;
   *(lds_ptr_t)(uintptr_t)addr = v;
-}
-
-// 16-byte LDS read at a byte address.
-__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
-  typedef __attribute__((address_space(3))) const bf16x8_t* lds_ptr_t;
-  return *(lds_ptr_t)(uintptr_t)addr;
 }
 
 // A lane's value and the value of lane l ^ 32.  With both operands holding v,
@@ -380,15 +342,12 @@ void fa_fwd_kernel(FwdParams p) {
   bf16x8_t ring[kRing];
   // K operand kk: rows 32*(kk%2) + r32, k-step kk/2 of the tile at ks.
   auto k_opnd = [&](uint32_t ks, int kk) -> bf16x8_t {
-    return lds_read16((ks ^ (32u * (kk >> 1))) + 2 * 32 * (kk & 1) * D);
+    return lds_read_bf16x8((ks ^ (32u * (kk >> 1))) + 2 * 32 * (kk & 1) * D);
   };
   // V^T operand j: block db = j%ND, k-step j/ND of the tile at vs (two transposing reads).
   auto v_opnd = [&](uint32_t vs, int j) -> bf16x8_t {
     const uint32_t base = (vs ^ (64u * (j % ND))) + 2 * 16 * (j / ND) * D;
-    const u32x2_t lo = lds_read_tr(base);
-    const u32x2_t hi = lds_read_tr(base + 2 * 8 * D);
-    const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-    return as_bf16x8(w);
+    return lds_read_tr_pair(base, base + 2 * 8 * D);
   };
   auto k_at = [&](int st) { return k_base + (uint32_t)st * kTileBytes; };
   auto v_at = [&](int st) { return v_base + (uint32_t)st * kTileBytes; };
@@ -683,15 +642,24 @@ hipError_t launch(const FwdLaunch& a, hipStream_t stream) {
   p.v_b = a.v_s[0]; p.v_h = a.v_s[1]; p.v_t = (uint32_t)a.v_s[2];
   p.o_b = a.o_s[0]; p.o_h = a.o_s[1]; p.o_t = (uint32_t)a.o_s[2];
   // One workgroup per CU (each needs a whole CU's LDS), in 8 groups (one per XCD) when there
-  // are more block pairs than CUs; otherwise one workgroup per pair.
+  // are more block pairs than CUs; otherwise one workgroup per pair.  The kernel looks two tiles
+  // ahead in its stream and resolves a stream position only within the current and the next
+  // item, so a workgroup that runs three or more items needs every item after its first to
+  // have at least two tiles.  Items have a single tile only when Tk <= kBN (every causal block
+  // with Tk > kBN sees at least min(Tk, 256) keys); those shapes take one workgroup per pair,
+  // i.e. at most two items per workgroup.
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const long long pairs = (long long)p.BH * p.npairs;
+  const bool single_tile_items = a.Tk <= kBN;
   int grid;
-  if (pairs > cus && cus >= 8) {
+  if (single_tile_items) {
+    p.groups = 1;
+    grid = (int)pairs;
+  } else if (pairs > cus && cus >= 8) {
     p.groups = 8;
     grid = cus - cus % 8;
   } else {

@@ -26,6 +26,40 @@ bool strides_ok(const int64_t* s, int64_t T, int64_t d, int64_t B, int64_t h) {
   return true;
 }
 
+// An output written by many workgroups must not alias itself: with its dimensions of extent > 1
+// ordered by stride, each stride must step past everything the smaller ones span (the usual
+// sufficient condition for a non-overlapping strided tensor; gaps between rows or heads are
+// allowed, interleavings that this order cannot express are rejected).  Inputs may broadcast
+// (stride 0, e.g. one K/V head shared by several query heads); outputs may not.
+bool no_self_overlap(const int64_t* stride, const int64_t* extent, int n) {
+  int64_t s[4], e[4];
+  int m = 0;
+  for (int i = 0; i < n; ++i)
+    if (extent[i] > 1) {
+      s[m] = stride[i];
+      e[m] = extent[i];
+      ++m;
+    }
+  for (int i = 1; i < m; ++i)   // insertion sort by stride
+    for (int j = i; j > 0 && s[j] < s[j - 1]; --j) {
+      const int64_t ts = s[j], te = e[j];
+      s[j] = s[j - 1]; e[j] = e[j - 1];
+      s[j - 1] = ts; e[j - 1] = te;
+    }
+  int64_t span = 0;   // largest element offset reachable through the dimensions so far
+  for (int i = 0; i < m; ++i) {
+    if (s[i] <= span) return false;
+    span += (e[i] - 1) * s[i];   // strides and extents were bounded by the callers' checks
+  }
+  return true;
+}
+
+// A [B][h][T][d] output with element strides s (batch, head, row) and a contiguous last dim.
+bool output4_ok(const int64_t* s, int64_t B, int64_t h, int64_t T, int64_t d) {
+  const int64_t stride[4] = {s[0], s[1], s[2], 1}, extent[4] = {B, h, T, d};
+  return no_self_overlap(stride, extent, 4);
+}
+
 // Per-head tensors are addressed with 32-bit byte offsets inside the kernels.
 bool head_bytes_ok(int64_t rows, int64_t d) {
   // one extra 128-row block of zero-filled reads past the end must still fit in 32 bits
@@ -46,6 +80,7 @@ extern "C" int fa_validate_fwd_strided(const void* q, const void* k, const void*
   if (!strides_ok(q_strides, Tq, d_head, B, h) || !strides_ok(k_strides, Tk, d_head, B, h) ||
       !strides_ok(v_strides, Tk, d_head, B, h) || !strides_ok(o_strides, Tq, d_head, B, h))
     return FA_ERR_SHAPE;
+  if (!output4_ok(o_strides, B, h, Tq, d_head)) return FA_ERR_SHAPE;
   const int64_t nqb = (Tq + 127) / 128;
   if (B > INT32_MAX / h || B * h > INT32_MAX / nqb) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SCALE;
@@ -64,7 +99,8 @@ extern "C" int fa_validate_fwd(const void* q, const void* k, const void* v, cons
   if (B < 1 || h < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
   if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!head_bytes_ok(Tq, d_head) || !head_bytes_ok(Tk, d_head)) return FA_ERR_SHAPE;
-  // the grid is one workgroup per (128-row query block, head, batch) and must fit in 31 bits
+  // (batch, head, query block) counts are kept in 32-bit integers on the device and the grid
+  // may run one workgroup per pair of query blocks: the count at 128-row granularity bounds both
   const int64_t nqb = (Tq + 127) / 128;
   if (B > INT32_MAX / h || B * h > INT32_MAX / nqb) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_SCALE;
@@ -127,6 +163,10 @@ extern "C" int fa_validate_decode_strided(const void* q, const void* k, const vo
   if (B < 1 || h < 1 || Tk < 1) return FA_ERR_SHAPE;
   if (!head_dim_ok(d_head)) return FA_ERR_HEAD_DIM;
   if (!strides2_ok(q_strides, B, h) || !strides2_ok(o_strides, B, h)) return FA_ERR_SHAPE;
+  {
+    const int64_t stride[3] = {o_strides[0], o_strides[1], 1}, extent[3] = {B, h, d_head};
+    if (!no_self_overlap(stride, extent, 3)) return FA_ERR_SHAPE;
+  }
   // the split pass reads up to 256 rows past a chunk's end (zero-filled), so one more block
   if (!strides_ok(k_strides, Tk + 128, d_head, B, h) ||
       !strides_ok(v_strides, Tk + 128, d_head, B, h))
@@ -194,6 +234,9 @@ extern "C" int fa_validate_bwd_strided(
       !strides_ok(do_strides, Tq, d_head, B, h) || !strides_ok(dq_strides, Tq, d_head, B, h) ||
       !strides_ok(k_strides, Tk, d_head, B, h) || !strides_ok(v_strides, Tk, d_head, B, h) ||
       !strides_ok(dk_strides, Tk, d_head, B, h) || !strides_ok(dv_strides, Tk, d_head, B, h))
+    return FA_ERR_SHAPE;
+  if (!output4_ok(dq_strides, B, h, Tq, d_head) || !output4_ok(dk_strides, B, h, Tk, d_head) ||
+      !output4_ok(dv_strides, B, h, Tk, d_head))
     return FA_ERR_SHAPE;
   const int64_t nb = ((Tq > Tk ? Tq : Tk) + 127) / 128;
   if (B > INT32_MAX / h || B * h > INT32_MAX / nb) return FA_ERR_SHAPE;

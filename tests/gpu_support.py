@@ -24,6 +24,27 @@ def to_gpu(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def lse_row_tolerance(q64: np.ndarray, k64: np.ndarray, scale: float, causal: bool,
+                      lse_ref: np.ndarray) -> np.ndarray:
+    """Absolute per-row LSE tolerance for scores far from O(1), from fp32 score rounding.
+
+    The kernels form s_ij = q_i . k_j in fp32 (bf16 products are exact; each of the d additions
+    rounds, so |ds_ij| <= d u A_ij with A_ij = sum_c |q_ic k_jc| and u = 2^-24, whatever the
+    summation order), then scale it, take the max and carry m + log l, each one fp32 rounding of
+    a value of magnitude <= |scale| A_ij or |LSE_i|.  Since dLSE_i/dS_ij = P_ij >= 0 sums to one,
+    |dLSE_i| <= max_j |dS_ij| over the visible keys.  Tolerance:
+        LSE_TOL + (d + 4) u |scale| max_j A_ij + 4 u |LSE_i|.
+    At O(1) scores the extra terms are ~1e-5 and LSE_TOL alone governs."""
+    u = 2.0 ** -24
+    d = q64.shape[-1]
+    A = np.abs(q64) @ np.abs(k64).T
+    if causal:
+        Tq, Tk = A.shape
+        vis = np.arange(Tk)[None, :] <= np.arange(Tq)[:, None] + (Tk - Tq)
+        A = np.where(vis, A, 0.0)
+    return LSE_TOL + (d + 4) * u * abs(float(scale)) * A.max(axis=1) + 4 * u * np.abs(lse_ref)
+
+
 def rne_bf16_of(t32: torch.Tensor) -> torch.Tensor:
     return t32.to(torch.bfloat16)
 

@@ -236,14 +236,24 @@ def _vs(fa_lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0),
-    ({"d": 128, "qs": (0, 0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 0, 128)}, 0),
+    # broadcast inputs (one q, k, v head for every batch and head) are fine ...
+    ({"d": 128, "qs": (0, 0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128),
+      "os": (3 * 100 * 128, 100 * 128, 128)}, 0),
+    # ... a broadcast or self-overlapping output is not: several workgroups would write one element
+    ({"d": 128, "qs": (0, 0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 0, 128)}, 2),
+    ({"os": (0, 100 * 80, 80)}, 2),                  # batches share the output
+    ({"os": (3 * 100 * 80, 50 * 80, 80)}, 2),        # heads overlap by 50 rows
+    ({"os": (3 * 100 * 80, 100 * 80, 40)}, 2),       # row stride below d is caught as well
+    ({"os": (100 * 3 * 80, 80, 3 * 80)}, 0),         # [B][T][h][d] output
+    ({"os": (80, 2 * 100 * 80, 2 * 80)}, 0),         # [h][T][B][d] output: interleaved, no overlap
+    ({"os": (80, 100 * 80, 80)}, 2),                 # batch stride inside a row's span
     ({"qs": None}, 2),
     ({"ks": (120 * 3 * 80, 80, 72)}, 2),            # row stride below d
     ({"ks": (120 * 3 * 80, 80, 3 * 80 + 4)}, 2),    # row stride not a multiple of 8
     ({"vs": (120 * 3 * 80, 84, 3 * 80)}, 2),        # head stride not a multiple of 8
     ({"os": (-8, 100 * 80, 80)}, 2),                # negative stride
     ({"ks": (0, 0, 2**26)}, 2),                      # head beyond 2^31 bytes
-    ({"d": 100}, 3), ({"Tq": 121}, 4),
+    ({"d": 100}, 3), ({"Tq": 121, "os": (3 * 121 * 80, 121 * 80, 80)}, 4),
 ])
 def test_validate_fwd_strided(fa_lib, kw, code):
     assert _vs(fa_lib, **kw) == code
@@ -267,14 +277,23 @@ _QS, _KS = (3 * 100 * 80, 80, 3 * 80), (3 * 120 * 80, 80, 3 * 80)
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0),
-    ({"d": 64, "strides": [(0, 0, 64)] * 8}, 0),
-    ({"d": 8, "strides": [(0, 0, 8)] * 8}, 0),
+    ({"d": 64, "strides": [(0, 0, 64)] * 5 + [(3 * 100 * 64, 100 * 64, 64)] +
+      [(3 * 120 * 64, 120 * 64, 64)] * 2}, 0),       # broadcast inputs, distinct gradients
+    ({"d": 8, "strides": [(0, 0, 8)] * 5 + [_QS, _KS, _KS]}, 0),
+    # a broadcast or self-overlapping gradient tensor is rejected
+    ({"d": 64, "strides": [(0, 0, 64)] * 8}, 2),
+    ({"strides": [_QS, _KS, _KS, _QS, _QS, (0, 80, 3 * 80), _KS, _KS]}, 2),     # dq batches alias
+    ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, (3 * 120 * 80, 0, 3 * 80), _KS]}, 2),  # dk heads
+    ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, _KS, (3 * 120 * 80, 80, 80)]}, 2),   # dv rows
+    # packed gradients ([B][T][3][h][d], dq/dk/dv interleaved) do not alias themselves
+    ({"Tk": 100, "strides": [_QS] * 5 + [(300 * 3 * 80, 80, 9 * 80)] * 3}, 0),
     ({"lse": 0}, 1), ({"dk": 0}, 1),
     ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, _KS, None]}, 2),
     ({"strides": [_QS, _KS, _KS, _QS, (3 * 100 * 80, 80, 72), _QS, _KS, _KS]}, 2),   # do row < d
     ({"strides": [_QS, _KS, _KS, _QS, _QS, _QS, (3 * 120 * 80, 84, 3 * 80), _KS]}, 2),
     ({"strides": [_QS, (0, 0, 2**26), _KS, _QS, _QS, _QS, _KS, _KS]}, 2),   # k head > 2^31 B
-    ({"d": 100}, 3), ({"d": 136}, 3), ({"Tq": 121}, 4),
+    ({"d": 100}, 3), ({"d": 136}, 3),
+    ({"Tq": 121, "strides": [_QS, _KS, _KS, _QS, _QS, (3 * 121 * 80, 80, 3 * 80), _KS, _KS]}, 4),
     ({"lse": P + 2}, 5), ({"dk": P + 8}, 5),
     ({"causal": 2}, 6), ({"ws_bytes": 16}, 8),
 ])
@@ -311,7 +330,10 @@ def _vds(fa_lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0),
-    ({"d": 128, "qs": (0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 128)}, 0),
+    ({"d": 128, "qs": (0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (3 * 128, 128)}, 0),
+    ({"d": 128, "qs": (0, 128), "ks": (0, 0, 128), "vs": (0, 0, 128), "os": (0, 128)}, 2),
+    ({"os": (80, 80)}, 2), ({"os": (3 * 80, 40)}, 2),   # output rows alias
+    ({"os": (80, 2 * 80)}, 0),                          # [h][B][d] output
     ({"o": P + 2}, 0),                       # o needs only 2-byte alignment
     ({"o": 0}, 1),
     ({"qs": None}, 2), ({"os": (3 * 80, 84)}, 2), ({"ks": (500 * 3 * 80, 80, 72)}, 2),

@@ -12,7 +12,7 @@ import torch
 import seeded_inputs as si
 from oracle import attention_ref as ref
 from tests.gpu_support import (LSE_TOL, O_TOL, assert_bf16_is_rne_of_f32, check_rows, log,
-                               run_fwd, to_gpu, workload_inputs)
+                               lse_row_tolerance, run_fwd, to_gpu, workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,6 +115,9 @@ def test_edge_shapes(gpu, B, h, Tq, Tk, d, causal):
 PERSISTENT_SHAPES = [
     (3, 37, 1100, 1100, 128, True), (3, 37, 1100, 1500, 64, True),
     (2, 45, 1300, 1300, 128, False), (1, 130, 1024, 1024, 64, True),
+    # one key tile per item with more items than CUs (the launcher runs one block pair per
+    # workgroup there, so the two-tile lookahead never has to reach past the next item)
+    (8, 32, 4096, 64, 128, False), (32, 32, 64, 64, 64, True), (8, 32, 4096, 40, 64, False),
 ]
 
 
@@ -126,10 +129,11 @@ def test_persistent_schedule_shapes(gpu, B, h, Tq, Tk, d, causal):
     assert_bf16_is_rne_of_f32(res)
     rng = np.random.default_rng(B * 1000 + h)
     edge = np.array([0, 1, 255, 256, 511, 512, Tq // 2, Tq - 2, Tq - 1])
+    edge = edge[edge < Tq]
     heads = {}
     for bh in sorted({0, 1, 7, 8, 9, B * h // 2, B * h - 2, B * h - 1} |
                      set(rng.choice(B * h, 8, replace=False).tolist())):
-        rows = np.unique(np.concatenate([edge, rng.choice(Tq, 24, replace=False)]))
+        rows = np.unique(np.concatenate([edge, rng.choice(Tq, min(Tq, 24), replace=False)]))
         heads[divmod(int(bh), h)] = rows
     _check_sampled(f"persistent B{B} h{h} Tq{Tq} Tk{Tk} d{d} causal{int(causal)}", res, q, k, v,
                    wl, heads)
@@ -229,8 +233,15 @@ def test_large_scores_stay_finite_and_exact(gpu, d):
     l32 = res["lse32"].cpu().numpy()
     for bh in heads:
         assert np.max(np.abs(o32[bh] - refs[bh][0])) <= O_TOL
-        # |LSE| ~ 1e2 here: allow fp32 relative rounding of the score itself
-        assert np.max(np.abs(l32[bh] - refs[bh][1]) / np.maximum(1, np.abs(refs[bh][1]))) <= LSE_TOL
+        # |LSE| reaches several hundred here: the gate is absolute per row, LSE_TOL plus the fp32
+        # rounding of scores of that size (lse_row_tolerance)
+        tol = lse_row_tolerance(si.bf16_bits_to_f64(q[bh]), si.bf16_bits_to_f64(k[bh]), scale,
+                                True, refs[bh][1])
+        err = np.abs(l32[bh] - refs[bh][1])
+        log(f"[parity] large scores d={d} head {bh}: max|LSE|={np.max(np.abs(refs[bh][1])):.1f} "
+            f"max|dLSE|={np.max(err):.3e} max tol={np.max(tol):.3e} worst ratio "
+            f"{np.max(err / tol):.3f}")
+        assert np.all(err <= tol)
 
 
 def test_run_to_run_bit_identical(gpu):

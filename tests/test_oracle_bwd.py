@@ -118,3 +118,27 @@ def test_batched_wrapper_matches_heads():
     r = bref.backward_head(q[1, 2], k[1, 2], v[1, 2], do[1, 2], 0.5, True)
     assert np.array_equal(dq[1, 2], r["dq"]) and np.array_equal(dv[1, 2], r["dv"])
     assert np.array_equal(D[1, 2], r["D"])
+
+
+def test_abs_bounds_are_attained_by_single_term_gradients():
+    """Upper pin: where a gradient element is one product, or products of one sign, the bound
+    equals |gradient| exactly, so an inflated bound (a wrong factor, |dP| for |dS|, a dropped
+    probability) fails here.  One query row: dK_j = scale dS_1j q_1 and dV_j = P_1j dO_1 are
+    single products.  Two keys with k_2 = -k_1: dS_i2 = -dS_i1, so dQ_i = 2 scale dS_i1 k_1 and
+    |dQ_i| = |scale| (|dS_i1| + |dS_i2|) |k_1|, the bound."""
+    d, scale = 5, -0.7
+    q, v, do = _rand(1, d), _rand(2, d), _rand(1, d)
+    k1 = _rand(1, d)
+    k = np.concatenate([k1, -k1])
+    r = bref.backward_head(q, k, v, do, scale, False)
+    a = bref.abs_bounds_head(r, q, k, do, scale)
+    for name in ("dq", "dk", "dv"):
+        assert np.all(np.abs(a[name]) > 0)
+        assert np.allclose(np.abs(r[name]), a[name], rtol=1e-12, atol=0), name
+    # several query rows, same-sign upstream gradients: A_dv = P^T |dO| = dV exactly
+    Tq, Tk = 7, 9
+    q, k, v = _rand(Tq, d), _rand(Tk, d), _rand(Tk, d)
+    do = np.abs(_rand(Tq, d))
+    r = bref.backward_head(q, k, v, do, scale, True)
+    a = bref.abs_bounds_head(r, q, k, do, scale)
+    assert np.allclose(r["dv"], a["dv"], rtol=1e-12, atol=0)
