@@ -20,6 +20,14 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
              values; a 4096 x 8192 bf16 activation with p = 0.1), timed separately: HBM GB/s
   layouts  = the forward on strided [B][T][h][d] inputs at the prefill shape, and at d_head = 80
              (20 heads, padded to 128 on chip), timed separately: TFLOP/s of the true d_head
+  configs  = every forward configuration with its roofline and the oracle timed beside it:
+             C1 (B=1 h=2 T=128 d=64 non-causal) as a latency; C2 (B=8 h=32 T=1024 d=64 causal)
+             against both the MFMA and the HBM peak, warm and with a 512 MB flush between
+             trials; C3 (the prefill above); C4 (B=2 h=32 T=16384 d=128 causal, 1% of keys x8)
+             against the MFMA peak; C5 (the decode above)
+  clock    = the GFX clock sampled (amdsmi) while the forward runs back to back, the CU count,
+             and the forward's fraction of the MFMA peak at that clock
+  host     = the CPUs the oracle ran on (affinity count, machine count, model, BLAS, threads)
 """
 from __future__ import annotations
 
@@ -74,6 +82,141 @@ def traffic_from_profiles(name):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
         return None
+
+
+def blas_threads():
+    """(vendor, threads) of the BLAS numpy's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            return (f"{pools[0].get('internal_api')} {pools[0].get('version')}",
+                    int(max(p.get("num_threads", 1) for p in pools)))
+    except Exception:  # pragma: no cover
+        pass
+    return ("unknown", os.cpu_count() or 1)
+
+
+def host_info():
+    """The host the CPU oracle runs on: CPUs visible to this process, CPUs of the machine, the
+    CPU model and the BLAS numpy uses."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    vendor, threads = blas_threads()
+    return {"affinity_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "cpu_model": model, "blas": vendor, "blas_threads": threads}
+
+
+def oracle_runs(wl, heads, runs, get_head=None):
+    """Seconds per run of the fp64 oracle over the listed (b, h) heads of a workload (input
+    generation and the bf16 -> fp64 conversion are outside the timed region)."""
+    import seeded_inputs as si
+    from oracle import attention_ref as ref
+    get_head = get_head or (lambda b, h: si.head_inputs(wl, 0, b, h))
+    cached = [tuple(si.bf16_bits_to_f64(x) for x in get_head(b, h)) for b, h in heads]
+    times = []
+    for _ in range(runs):
+        el = 0.0
+        for q, k, v in cached:
+            q2 = q.reshape(-1, wl.d)
+            t0 = time.perf_counter()
+            ref.naive_attention_head(q2, k, v, wl.scale, wl.causal)
+            el += time.perf_counter() - t0
+        times.append(el)
+    return times
+
+
+def oracle_baseline(wl, heads, runs, what, unit="TFLOP/s", get_head=None):
+    """The oracle timed on a sample of heads, scaled to the metric's unit: TFLOP/s by the same
+    FLOP formula as the GPU, or GB/s of K+V (decode)."""
+    from io_aware_attention_fa_amd import costmodel as cm
+    times = oracle_runs(wl, heads, runs, get_head)
+    n = len(heads)
+    if unit == "GB/s":
+        work = n * wl.Tk * cm.decode_kv_bytes_per_token(wl.d) / 1e9
+    else:
+        work = cm.attention_flops(1, n, wl.Tq, wl.Tk, wl.d, wl.causal) / 1e12
+    best = min(times)
+    return {"value": work / best, "unit": unit, "cores": blas_threads()[1], "kind": "oracle",
+            "runs_s": times, "seconds_per_head": best / n,
+            "seconds_whole_workload_est": best / n * wl.B * wl.h,
+            "sample": f"{n} of {wl.B * wl.h} heads of {wl.name}, {what}; {runs} run(s), best "
+                      f"of {best:.3g} s of fp64 numpy"}
+
+
+def sample_clock(torch, fn, seconds=1.5):
+    """The GFX clock while fn runs back to back: amdsmi's gpu_metrics of this device sampled from
+    a host thread every few ms over about ``seconds`` of launches (outside any timed region).
+    Returns None if the metrics cannot be read."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # pragma: no cover
+        return {"mhz": None, "error": f"amdsmi unavailable: {e}"}
+    try:
+        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        hnd = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(hnd)
+            xs = m.get("current_gfxclks")
+            if isinstance(xs, (list, tuple)):
+                xs = [x for x in xs if isinstance(x, (int, float)) and 0 < x < 10000]
+                if xs:
+                    return sum(xs) / len(xs)
+            x = m.get("current_gfxclk")
+            return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+        if read() is None:
+            return {"mhz": None, "error": "gpu_metrics hold no current GFX clock"}
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                v = read()
+                if v is not None:
+                    samples.append(v)
+                time.sleep(0.004)
+
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 0.3:   # calls per batch: about 0.3 s of work
+            fn()
+            n += 1
+            torch.cuda.synchronize()
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return {"mhz": None, "error": "no samples"}
+        samples.sort()
+        return {"mhz": sum(samples) / len(samples), "median_mhz": samples[len(samples) // 2],
+                "samples": len(samples), "bdf": bdf,
+                "source": "amdsmi gpu_metrics current GFX clock (mean over XCDs), sampled "
+                          "every ~4 ms during back-to-back launches"}
+    except Exception as e:  # pragma: no cover
+        return {"mhz": None, "error": f"{type(e).__name__}: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def cpu_baseline(seconds_budget: float):
@@ -179,6 +322,138 @@ def measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse):
     if not args.no_cpu_baseline:
         eprint("[bench] timing the CPU backward oracle on a sample")
         res["cpu_baseline"] = cpu_baseline_backward(min(args.cpu_seconds, 15.0))
+    return res
+
+
+def event_trials(torch, fn, warmup, trials, between=None):
+    """Per-call durations (ms) of fn from HIP events recorded around each call on the launch
+    stream; ``between`` (if given) is enqueued before each trial, outside its events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(trials)]
+    for a, b in ev:
+        if between is not None:
+            between()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"avg_ms": sum(t) / trials, "median_ms": t[trials // 2], "min_ms": t[0],
+            "trials": trials}
+
+
+def rooflines(cm, flops, nbytes, ms):
+    """Achieved rates of one launch against the MFMA and the HBM peaks."""
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    pf = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
+    pb = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
+    return ({"bound": "mfma", "achieved": tf, "peak": pf, "unit": "TFLOP/s", "frac": tf / pf,
+             "traffic": None},
+            {"bound": "hbm", "achieved": gbs, "peak": pb, "unit": "GB/s", "frac": gbs / pb,
+             "traffic": None})
+
+
+def measure_configs(args, fa, si, cm, torch):
+    """The other forward configurations: the tiny non-causal case as a latency, B=8 h=32 T=1024
+    d=64 causal against both rooflines (it sits near the ridge) with and without a 512 MB cache
+    flush between trials, and the long-context B=2 h=32 T=16384 d=128 causal workload with key
+    spikes as a fraction of the MFMA peak; each with the CPU oracle timed beside it."""
+    res = {}
+    cpu = not args.no_cpu_baseline
+    # C1: latency of one call, and of 20 back-to-back calls between two events
+    wl = si.WORKLOADS["tiny_noncausal_b1_h2_t128_d64"]
+    q, k, v = si.make_inputs(wl, seed=0, threads=2)
+    tq, tk, tv = upload(q), upload(k), upload(v)
+    o = torch.empty_like(tq)
+    lse = torch.empty((wl.B, wl.h, wl.Tq), dtype=torch.float32, device="cuda")
+    call = lambda: fa.fa_fwd(tq, tk, tv, causal=False, scale=wl.scale, o=o, lse=lse)
+    t = event_trials(torch, call, 20, 200)
+    t["back_to_back_20_avg_ms"] = time_calls(torch, call, 5, 20)
+    flops = cm.attention_flops(1, 2, 128, 128, 64, False)
+    nbytes = cm.attention_io_bytes(1, 2, 128, 128, 64)
+    r_f, r_b = rooflines(cm, flops, nbytes, t["median_ms"])
+    c1 = {"metric": "attention fwd latency (one call, HIP events around the launch)",
+          "value": t["median_ms"] * 1e3, "unit": "us", "higher_is_better": False,
+          "roofline": {"bound": "latency", "achieved": t["median_ms"] * 1e3, "peak": None,
+                       "unit": "us", "frac": None, "traffic": None,
+                       "mfma_frac": r_f["frac"], "hbm_frac": r_b["frac"]},
+          "timing": t, "config": {"workload": wl.name, "flops": flops, "alg_bytes": nbytes}}
+    eprint(f"[bench] C1 {wl.name}: median {t['median_ms'] * 1e3:.1f} us per call, "
+           f"{t['back_to_back_20_avg_ms'] * 1e3:.1f} us back to back")
+    if cpu:
+        c1["cpu_baseline"] = oracle_baseline(wl, [(0, 0), (0, 1)], 3, "whole workload")
+        cb = c1["cpu_baseline"]
+        cb["latency_ms"] = min(cb["runs_s"]) * 1e3
+    res["C1"] = c1
+    del tq, tk, tv, o, lse
+
+    # C2: near the ridge; warm (inputs resident in the 256 MB MALL) and with a 512 MB write
+    # between trials
+    wl = si.WORKLOADS["causal_b8_h32_t1024_d64"]
+    q, k, v = si.make_inputs(wl, seed=0)
+    tq, tk, tv = upload(q), upload(k), upload(v)
+    del q, k, v
+    o = torch.empty_like(tq)
+    lse = torch.empty((wl.B, wl.h, wl.Tq), dtype=torch.float32, device="cuda")
+    call = lambda: fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse)
+    warm = event_trials(torch, call, 10, 100)
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
+    cnt = [0]
+
+    def scrub():
+        cnt[0] += 1
+        flush.fill_(cnt[0] & 0xff)
+
+    cold = event_trials(torch, call, 3, 100, between=scrub)
+    del flush
+    flops = cm.attention_flops(wl.B, wl.h, wl.Tq, wl.Tk, wl.d, True)
+    nbytes = cm.attention_io_bytes(wl.B, wl.h, wl.Tq, wl.Tk, wl.d)
+    w_f, w_b = rooflines(cm, flops, nbytes, warm["avg_ms"])
+    c_f, c_b = rooflines(cm, flops, nbytes, cold["avg_ms"])
+    c2 = {"metric": "attention fwd TFLOP/s and HBM GB/s at the ridge (causal T=1024 d=64)",
+          "value": w_f["achieved"], "unit": "TFLOP/s", "roofline": w_b,
+          "roofline_mfma": w_f, "roofline_hbm": w_b, "timing": warm,
+          "flushed": {"timing": cold, "roofline_mfma": c_f, "roofline_hbm": c_b,
+                      "flush": "512 MB device write between trials (outside the events)"},
+          "config": {"workload": wl.name, "flops": flops, "alg_bytes": nbytes}}
+    eprint(f"[bench] C2 {wl.name}: {warm['avg_ms'] * 1e3:.1f} us  {w_f['achieved']:.0f} TFLOP/s "
+           f"({100 * w_f['frac']:.1f}% MFMA)  {w_b['achieved']:.0f} GB/s "
+           f"({100 * w_b['frac']:.1f}% HBM); flushed {cold['avg_ms'] * 1e3:.1f} us "
+           f"({100 * c_f['frac']:.1f}% MFMA, {100 * c_b['frac']:.1f}% HBM)")
+    if cpu:
+        c2["cpu_baseline"] = oracle_baseline(wl, [divmod(i, wl.h) for i in range(0, 256, 4)], 3,
+                                             "every 4th head")
+    res["C2"] = c2
+    del tq, tk, tv, o, lse
+    torch.cuda.empty_cache()
+
+    # C4: long context with key spikes
+    wl = si.WORKLOADS["longctx_causal_b2_h32_t16384_d128_keyspikes"]
+    q, k, v = si.make_inputs(wl, seed=0)
+    tq, tk, tv = upload(q), upload(k), upload(v)
+    del q, k, v
+    o = torch.empty_like(tq)
+    lse = torch.empty((wl.B, wl.h, wl.Tq), dtype=torch.float32, device="cuda")
+    call = lambda: fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse)
+    t = event_trials(torch, call, 3, max(20, args.extra_steps))
+    flops = cm.attention_flops(wl.B, wl.h, wl.Tq, wl.Tk, wl.d, True)
+    nbytes = cm.attention_io_bytes(wl.B, wl.h, wl.Tq, wl.Tk, wl.d)
+    r_f, r_b = rooflines(cm, flops, nbytes, t["avg_ms"])
+    c4 = {"metric": "attention fwd TFLOP/s (% MFMA peak), causal T=16384 d=128, 1% keys x8",
+          "value": r_f["achieved"], "unit": "TFLOP/s", "roofline": r_f, "roofline_hbm": r_b,
+          "timing": t, "config": {"workload": wl.name, "flops": flops, "alg_bytes": nbytes}}
+    eprint(f"[bench] C4 {wl.name}: {t['avg_ms']:.3f} ms  {r_f['achieved']:.0f} TFLOP/s "
+           f"({100 * r_f['frac']:.1f}% MFMA)")
+    if cpu:
+        c4["cpu_baseline"] = oracle_baseline(wl, [(0, 0), (0, 11), (1, 5), (1, 30)], 1,
+                                             "four whole heads")
+    res["C4"] = c4
+    del tq, tk, tv, o, lse
+    torch.cuda.empty_cache()
     return res
 
 
@@ -427,7 +702,12 @@ def main():
                     help="timed calls of each separately measured kernel (0: its default)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the separately timed softmax and elementwise measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other forward configurations (T=128 latency, T=1024 at the "
+                         "ridge, T=16384 long context)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the GFX clock under the forward")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -511,6 +791,7 @@ def main():
         po = torch.empty_like(pq)
         plse = torch.empty((wp.B, wp.h, wp.Tq), dtype=torch.float32, device="cuda")
         del q, k, v
+    dec_host = None
     if do_decode:
         q, k, v = si.make_inputs(wd, seed=0)
         dq, dk, dv = upload(q), upload(k), upload(v)
@@ -518,6 +799,8 @@ def main():
         dlse = torch.empty((wd.B, wd.h), dtype=torch.float32, device="cuda")
         ws = torch.empty(fa.fa_decode_workspace_size(wd.B, wd.h, wd.d, wd.num_splits),
                          dtype=torch.uint8, device="cuda")
+        if not args.no_cpu_baseline:
+            dec_host = (q, k, v)   # the oracle's sample reads the same bits
         del q, k, v
     torch.cuda.synchronize()
     eprint(f"[bench] inputs generated and resident in {time.perf_counter() - t0:.1f} s")
@@ -607,12 +890,53 @@ def main():
         if not do_prefill:
             out.update(value=gbs, unit="GB/s", roofline=dec["roofline"])
     out["config"] = config
+    out["host"] = host_info()
+    cus = props.multi_processor_count
+    if do_prefill and not args.no_clock:
+        clk = sample_clock(torch, lambda: fa.fa_fwd(pq, pk, pv, causal=True, scale=wp.scale,
+                                                    o=po, lse=plse))
+        clk["cus"] = cus
+        clk["device"] = props.name
+        if clk.get("mhz"):
+            pk_clk = cm.bf16_peak_at_clock(clk["mhz"] * 1e6, cus) / 1e12
+            clk["mfma_peak_at_clock_tflops"] = pk_clk
+            clk["frac_at_clock"] = out["value"] / pk_clk
+            out["roofline"]["frac_at_clock"] = out["value"] / pk_clk
+            out["roofline"]["sclk_mhz"] = clk["mhz"]
+            eprint(f"[bench] GFX clock under the forward: {clk['mhz']:.0f} MHz mean "
+                   f"({clk['samples']} samples); MFMA peak at that clock {pk_clk:.0f} TFLOP/s, "
+                   f"forward at {100 * clk['frac_at_clock']:.1f}% of it")
+        else:
+            eprint(f"[bench] GFX clock not measured: {clk.get('error')}")
+        out["clock"] = clk
+    else:
+        out["clock"] = {"mhz": None, "cus": cus, "device": props.name}
 
     if do_prefill and not args.no_cpu_baseline:
         eprint("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    configs = {}
+    if do_prefill:
+        configs["C3"] = {"workload": PREFILL, "value": out["value"], "unit": "TFLOP/s",
+                         "roofline": out["roofline"], "cpu_baseline": out["cpu_baseline"]}
+    if do_decode:
+        c5 = {"workload": DECODE, "value": out["decode"]["value"], "unit": "GB/s",
+              "roofline": out["decode"]["roofline"]}
+        if dec_host is not None:
+            eprint("[bench] timing the CPU decode oracle on a sample")
+            hq, hk, hv = dec_host
+            c5["cpu_baseline"] = oracle_baseline(
+                wd, [divmod(i, wd.h) for i in range(0, wd.B * wd.h, 16)], 3, "every 16th head",
+                unit="GB/s", get_head=lambda b, h: (hq[b, h], hk[b, h], hv[b, h]))
+            out["decode"]["cpu_baseline"] = c5["cpu_baseline"]
+            del hq, hk, hv, dec_host
+        configs["C5"] = c5
+    if args.only is None and not args.no_configs:
+        configs.update(measure_configs(args, fa, si, cm, torch))
+    if configs:
+        out["configs"] = configs
     if do_backward:
         out["backward"] = measure_backward(args, fa, si, cm, torch, wp, pq, pk, pv, po, plse)
     if do_softmax:
