@@ -55,7 +55,8 @@ enum {
   FA_ERR_SPLITS = 7,           /* num_splits outside [1, min(Tk, FA_MAX_SPLITS)]                */
   FA_ERR_WORKSPACE = 8,        /* decode workspace NULL, misaligned or smaller than required     */
   FA_ERR_HIP = 9,              /* a HIP launch failed; see fa_last_hip_error()                  */
-  FA_ERR_PROB = 10             /* a dropout probability outside [0, 1)                          */
+  FA_ERR_PROB = 10,            /* a dropout probability outside [0, 1)                          */
+  FA_ERR_SCRATCH = 11          /* fa_decode_noalloc: partials beyond FA_NOALLOC_SCRATCH_BYTES   */
 };
 
 /* Largest per-head tensor the kernels address with 32-bit byte offsets: T * d_head * 2 bytes
@@ -64,6 +65,8 @@ enum {
 #define FA_MAX_HEAD_BYTES 2147483647LL
 /* Largest split count of the decode entry point. */
 #define FA_MAX_SPLITS 256
+/* Size of the static per-GPU array that holds fa_decode_noalloc's partials (32 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES 33554432
 
 /*
  * fa_fwd -- attention forward (prefill).
@@ -140,6 +143,25 @@ size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t nu
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
               int64_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_noalloc -- fa_decode without a workspace argument, for callers that cannot allocate
+ *   device memory (code under graph capture, tight serving loops, harnesses that forbid
+ *   allocation).  The per-split partials go to a static array of FA_NOALLOC_SCRATCH_BYTES that
+ *   the library's code object holds on each GPU it runs on until the process ends; the call
+ *   itself allocates nothing.  Same arguments (less the workspace), kernels and results as
+ *   fa_decode, bit for bit.
+ *   Errors: as fa_decode, and FA_ERR_SCRATCH (nothing enqueued, outputs untouched) when
+ *   fa_decode_workspace_size(B, h, d_head, num_splits) exceeds FA_NOALLOC_SCRATCH_BYTES
+ *   (e.g. B = 64, h = 32, d_head = 128 allows up to 31 splits).  The first call on a device
+ *   looks up that device's address of the array (a HIP call; failure gives FA_ERR_HIP).
+ *   All calls on one GPU share its array: calls that overlap in time on one GPU (different
+ *   streams, or unordered threads) race on it and give undefined results.  Nothing in the
+ *   array needs clearing between calls: each call writes every partial it reads.
+ */
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
+                      int64_t num_splits, void* stream);
 
 /*
  * fa_decode_strided -- fa_decode on strided tensors and any head dim (layout variants).

@@ -14,10 +14,10 @@ import torch
 
 from . import _lib
 from ._lib import (FA_ERR_ALIGN, FA_ERR_CAUSAL_TQ_GT_TK, FA_ERR_HEAD_DIM, FA_ERR_HIP,  # noqa: F401
-                   FA_ERR_NULL, FA_ERR_PROB, FA_ERR_SCALE, FA_ERR_SHAPE, FA_ERR_SPLITS,
-                   FA_ERR_WORKSPACE, FA_OK, LIB_PATH)
+                   FA_ERR_NULL, FA_ERR_PROB, FA_ERR_SCALE, FA_ERR_SCRATCH, FA_ERR_SHAPE,
+                   FA_ERR_SPLITS, FA_ERR_WORKSPACE, FA_NOALLOC_SCRATCH_BYTES, FA_OK, LIB_PATH)
 
-__all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_workspace_size", "fa_decode_strided", "fa_validate_decode_strided", "fa_bwd",
+__all__ = ["fa_fwd", "fa_fwd_o32", "fa_fwd_strided", "fa_validate_fwd_strided", "fa_decode", "fa_decode_noalloc", "fa_decode_workspace_size", "fa_decode_strided", "fa_validate_decode_strided", "fa_bwd",
            "fa_bwd_f32", "fa_bwd_workspace_size", "fa_validate_fwd", "fa_validate_decode",
            "fa_validate_bwd", "fa_bwd_strided", "fa_validate_bwd_strided", "fa_softmax_rows", "fa_validate_softmax", "fa_gelu_f32",
            "fa_gelu_bf16", "fa_bias_gelu_dropout_bf16", "fa_validate_gelu",
@@ -202,6 +202,34 @@ def fa_decode(q, k, v, *, num_splits: int, scale: float | None = None, o=None, l
     st = _lib.lib.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, h, Tk, d, scale, int(num_splits), workspace.data_ptr(),
                             workspace.numel(), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def fa_decode_noalloc(q, k, v, *, num_splits: int, scale: float | None = None, o=None,
+                      lse=None, stream=None):
+    """:func:`fa_decode` with the partials in the library's static per-GPU array instead of a
+    workspace: the library allocates nothing (pass ``o`` and ``lse`` for an allocation-free
+    call).  Calls that overlap on one GPU race on that array.  FA_ERR_SCRATCH when the partials,
+    fa_decode_workspace_size(B, h, d, num_splits) bytes, exceed FA_NOALLOC_SCRATCH_BYTES."""
+    _check_tensor("q", q, torch.bfloat16, 3)
+    _check_tensor("k", k, torch.bfloat16, 4)
+    _check_tensor("v", v, torch.bfloat16, 4)
+    B, h, d = q.shape
+    Tk = k.shape[2]
+    if tuple(k.shape) != (B, h, Tk, d) or tuple(v.shape) != (B, h, Tk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o is None:
+        o = torch.empty((B, h, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = _lib.lib.fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, h, Tk, d, scale, int(num_splits),
+                                    _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FaError(st)
     return o, lse

@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_decode_workspace_size": (_size, [_i64, _i64, _i64, _i64]),
     "fa_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64, _vp, _size,
                          _vp]),
+    "fa_decode_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i64,
+                                 _vp]),
     "fa_validate_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _f32]),
     "fa_decode_strided": (_int, [_vp] * 5 + [_i64] * 4 + [_vp] * 4 + [_f32, _i64, _vp, _size,
                                                                        _vp]),
@@ -75,3 +77,5 @@ FA_ERR_SPLITS = 7
 FA_ERR_WORKSPACE = 8
 FA_ERR_HIP = 9
 FA_ERR_PROB = 10
+FA_ERR_SCRATCH = 11
+FA_NOALLOC_SCRATCH_BYTES = 33554432   # include/fa.h

@@ -22,7 +22,7 @@ LIB_NAME = "libfa_mi355x.so"
 
 SOURCES = ["fa_validate.cpp", "fa_host.cpp", "fa_fwd_kernel.hip", "fa_decode_kernel.hip",
            "fa_bwd_kernel.hip", "fa_softmax_kernel.hip",
-           "fa_elementwise_kernel.hip"]
+           "fa_elementwise_kernel.hip", "fa_noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are kept out of every kernel.

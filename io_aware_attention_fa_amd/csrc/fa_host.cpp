@@ -8,10 +8,14 @@
 
 namespace {
 thread_local int g_last_hip_error = 0;
+}  // namespace
 
+void fa::note_hip_error(int hip_error) { g_last_hip_error = hip_error; }
+
+namespace {
 int map_hip(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
-  g_last_hip_error = static_cast<int>(e);
+  fa::note_hip_error(static_cast<int>(e));
   return FA_ERR_HIP;
 }
 

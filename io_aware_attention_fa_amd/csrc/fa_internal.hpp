@@ -77,6 +77,9 @@ struct DropoutLaunch {
   uint64_t seed, offset;
 };
 
+// Records the hipError_t behind an FA_ERR_HIP for fa_last_hip_error() (per thread).
+void note_hip_error(int hip_error);
+
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);

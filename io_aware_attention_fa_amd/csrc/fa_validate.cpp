@@ -294,6 +294,9 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, misaligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed (see fa_last_hip_error)";
     case FA_ERR_PROB: return "FA_ERR_PROB: the dropout probability must be in [0, 1)";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the decode partials exceed the static scratch array "
+             "(FA_NOALLOC_SCRATCH_BYTES); use fewer splits or fa_decode with a workspace";
     default: return "unknown fa status code";
   }
 }

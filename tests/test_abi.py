@@ -44,7 +44,7 @@ def test_binding_covers_every_declared_function(fa_lib):
 
 def test_status_strings(fa_lib):
     seen = set()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa_lib.fa_status_str(code)
         assert s and s not in seen
         seen.add(s)
@@ -344,3 +344,23 @@ def _vds(fa_lib, **kw):
 ])
 def test_validate_decode_strided(fa_lib, kw, code):
     assert _vds(fa_lib, **kw) == code
+
+
+def test_noalloc_decode_rejects_before_any_hip_call(fa_lib):
+    """fa_decode_noalloc: argument errors and partials beyond the static array are reported before
+    the library touches the GPU, with every output untouched."""
+    from io_aware_attention_fa_amd import _lib
+    buf = np.zeros(64, dtype=np.uint16)
+    out = np.full(64, 0x7FC1, dtype=np.uint16)
+    lse = np.full(4, 5.0, dtype=np.float32)
+    a = [ctypes.c_void_p(x.ctypes.data) for x in (buf, buf, buf, out, lse)]
+    call = lambda B, h, Tk, d, S: _lib.lib.fa_decode_noalloc(*a, B, h, Tk, d, 0.125, S, None)
+    assert fa_lib.FA_NOALLOC_SCRATCH_BYTES == 32 * 2**20
+    # B=64, h=32, d=128: 31 splits fit in the array, 32 do not
+    assert fa_lib.fa_decode_workspace_size(64, 32, 128, 31) <= fa_lib.FA_NOALLOC_SCRATCH_BYTES
+    assert call(64, 32, 8192, 128, 32) == fa_lib.FA_ERR_SCRATCH
+    assert call(1, 1, 300, 128, 0) == fa_lib.FA_ERR_SPLITS
+    assert call(1, 1, 300, 100, 4) == fa_lib.FA_ERR_HEAD_DIM
+    assert _lib.lib.fa_decode_noalloc(None, *a[1:], 1, 1, 300, 128, 0.125, 4, None) == 1
+    assert np.all(out == 0x7FC1) and np.all(lse == 5.0)
+    assert "FA_NOALLOC_SCRATCH_BYTES" in fa_lib.fa_status_str(fa_lib.FA_ERR_SCRATCH)
