@@ -15,8 +15,8 @@
 //
 // MI355X mapping (our design): streaming kernels with 16-byte nontemporal loads and stores,
 // 4 (fp32) or 8 (bf16) elements per lane per access, several accesses in flight per lane; the
-// dropout kernel gives each lane 8 consecutive columns of one row (two Philox blocks) so that the
-// bias needs no division by the row length.  Lengths that do not fit the vector layout take a
+// dropout kernel gives each lane 8 consecutive columns of two rows (two Philox blocks per row)
+// so that the bias needs no division by the row length and is unpacked once for both rows.  Lengths that do not fit the vector layout take a
 // scalar path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,12 +32,12 @@ constexpr int kUnrollEw = 4;   // vector accesses in flight per lane
 
 // -2 sqrt(2/pi) log2(e) and the cubic coefficient: gelu(x) = x / (1 + 2^(K1 x (1 + A x^2)))
 constexpr float kGeluK1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
-constexpr float kGeluA = 0.044715f;
+constexpr float kGeluK1A = -2.0f * 0.7978845608028654f * 1.4426950408889634f * 0.044715f;
 
-// x / (1 + 2^z) with the hardware reciprocal (within an ulp or so; 1 + 2^z >= 1, and an
-// infinite 2^z gives 0, the limit).
+// x / (1 + 2^z) with z = x (K1 + K1 A x^2) and the hardware reciprocal (within an ulp or so;
+// 1 + 2^z >= 1, and an infinite 2^z gives 0, the limit).
 __device__ __forceinline__ float gelu(float x) {
-  const float z = x * kGeluK1 * __builtin_fmaf(kGeluA * x, x, 1.0f);
+  const float z = x * __builtin_fmaf(x * x, kGeluK1A, kGeluK1);
   return x * __builtin_amdgcn_rcpf(1.0f + fast_exp2(z));
 }
 
@@ -62,9 +62,10 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    c0 = hi1 ^ c1 ^ k0;
+    // three-input XORs as one gfx950 v_bitop3_b32 each (truth table 0x96: odd parity)
+    c0 = __builtin_amdgcn_bitop3_b32(hi1, c1, k0, 0x96);
     c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
+    c2 = __builtin_amdgcn_bitop3_b32(hi0, c3, k1, 0x96);
     c3 = lo0;
   }
   return Philox4{{c0, c1, c2, c3}};
@@ -152,14 +153,11 @@ __device__ __forceinline__ float dropout_one(float xb, uint32_t word, const Drop
   return word >= p.threshold ? g : 0.f;
 }
 
-// Vector path (cols % 8 == 0, 16-byte aligned rows): lane -> 8 consecutive columns of one row.
-__global__ __launch_bounds__(kThreadsEw) void fa_bias_gelu_dropout_vec_kernel(DropoutParams p) {
-  const int64_t row = blockIdx.y;
-  const int64_t col = ((int64_t)blockIdx.x * kThreadsEw + threadIdx.x) * 8;
-  if (col >= p.cols) return;
-  const int64_t e = row * p.cols + col;   // a multiple of 8
-  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.x + e));
-  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p.bias + col);
+// Vector path (cols % 8 == 0, 16-byte aligned rows): lane -> the same 8 consecutive columns of
+// two rows (2 * blockIdx.y and the next one, if any), so that the bias is loaded and unpacked once
+// and both rows' loads are in flight together.
+__device__ __forceinline__ u32x4_t dropout_8(u32x4_t a, const float (&bf)[8], int64_t e,
+                                            const DropoutParams& p) {
   const uint64_t blk = (uint64_t)e >> 2;
   const Philox4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.off_lo, p.off_hi,
                                    p.seed_lo, p.seed_hi);
@@ -170,13 +168,34 @@ __global__ __launch_bounds__(kThreadsEw) void fa_bias_gelu_dropout_vec_kernel(Dr
   for (int j = 0; j < 4; ++j) {
     const Philox4& w = j < 2 ? w0 : w1;
     const int k = (2 * j) & 3;
-    r[2 * j] = dropout_one(bf16_lo(a[j]) + bf16_lo(b[j]), w.v[k], p);
-    r[2 * j + 1] = dropout_one(bf16_hi(a[j]) + bf16_hi(b[j]), w.v[k + 1], p);
+    r[2 * j] = dropout_one(bf16_lo(a[j]) + bf[2 * j], w.v[k], p);
+    r[2 * j + 1] = dropout_one(bf16_hi(a[j]) + bf[2 * j + 1], w.v[k + 1], p);
   }
   const u32x2_t lo = pack_bf16x4(r[0], r[1], r[2], r[3]);
   const u32x2_t hi = pack_bf16x4(r[4], r[5], r[6], r[7]);
-  __builtin_nontemporal_store(u32x4_t{lo[0], lo[1], hi[0], hi[1]},
-                              reinterpret_cast<u32x4_t*>(p.y + e));
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__global__ __launch_bounds__(kThreadsEw) void fa_bias_gelu_dropout_vec_kernel(DropoutParams p) {
+  const int64_t row = 2 * (int64_t)blockIdx.y;
+  const int64_t col = ((int64_t)blockIdx.x * kThreadsEw + threadIdx.x) * 8;
+  if (col >= p.cols) return;
+  const bool two = row + 1 < p.rows;
+  const int64_t e = row * p.cols + col;   // a multiple of 8
+  const u32x4_t a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.x + e));
+  u32x4_t a1 = u32x4_t{0u, 0u, 0u, 0u};
+  if (two) a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.x + e + p.cols));
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p.bias + col);
+  float bf[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf[2 * j] = bf16_lo(b[j]);
+    bf[2 * j + 1] = bf16_hi(b[j]);
+  }
+  __builtin_nontemporal_store(dropout_8(a0, bf, e, p), reinterpret_cast<u32x4_t*>(p.y + e));
+  if (two)
+    __builtin_nontemporal_store(dropout_8(a1, bf, e + p.cols, p),
+                                reinterpret_cast<u32x4_t*>(p.y + e + p.cols));
 }
 
 // Scalar path: one element per lane, any shape.
@@ -233,7 +252,8 @@ hipError_t launch_bias_gelu_dropout(const DropoutLaunch& a, hipStream_t s) {
                    reinterpret_cast<uintptr_t>(a.bias) % 16 == 0 && a.rows <= 65535;
   if (vec) {
     const int64_t gx = (a.cols / 8 + kThreadsEw - 1) / kThreadsEw;
-    hipLaunchKernelGGL(fa_bias_gelu_dropout_vec_kernel, dim3((unsigned)gx, (unsigned)a.rows),
+    const int64_t gy = (a.rows + 1) / 2;   // row pairs
+    hipLaunchKernelGGL(fa_bias_gelu_dropout_vec_kernel, dim3((unsigned)gx, (unsigned)gy),
                        dim3(kThreadsEw), 0, s, p);
   } else {
     int64_t g = (a.rows * a.cols + kThreadsEw - 1) / kThreadsEw;

@@ -127,6 +127,8 @@ def _dropout_case(gpu, rows, cols, p, seed, offset, tag, sample_rows=None):
     (5, 1000, 0.1, 3, 2**33 + 7),           # vector path, offset above 32 bits
     (2, 1003, 0.9, 2**40 + 11, 1),          # scalar path, seed above 32 bits
     (6, 4096, 0.0, 9, 0),                   # p = 0: no drops
+    (1, 2048, 0.3, 4, 3),                   # vector path, one row (its pair has no second row)
+    (7, 24, 0.2, 6, 1),                     # vector path, odd row count, one lane per row
 ])
 def test_bias_gelu_dropout_shapes(gpu, rows, cols, p, seed, offset):
     log(f"[case] bias-gelu-dropout {rows}x{cols} p={p} seed={seed} offset={offset}")
