@@ -18,8 +18,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
              (one read and one write of the matrix) against the HBM peak
   gelu, bias_gelu_dropout = the fused elementwise chains on the pages' workloads (64M fp32
              values; a 4096 x 8192 bf16 activation with p = 0.1), timed separately: HBM GB/s
-  layouts  = the forward on strided [B][T][h][d] inputs at the prefill shape, and at d_head = 80
-             (20 heads, padded to 128 on chip), timed separately: TFLOP/s of the true d_head
+  layouts  = the forward and backward on strided [B][T][h][d] tensors at the prefill shape, each
+             timed in alternating rounds with the contiguous call (ratio reported), d_head = 80
+             (20 heads, padded to 128 on chip; TFLOP/s of the true and of the padded d_head),
+             and the decode on a [B][Tk][h][d] KV cache
   configs  = every forward configuration with its roofline and the oracle timed beside it:
              C1 (B=1 h=2 T=128 d=64 non-causal) as a latency; C2 (B=8 h=32 T=1024 d=64 causal)
              against both the MFMA and the HBM peak, warm and with a 512 MB flush between
@@ -512,83 +514,131 @@ def measure_softmax(args, fa, si, torch):
     return res
 
 
+def interleaved(torch, fns, warmup, steps, rounds=5):
+    """Median per-call milliseconds of each of several calls, timed in alternating rounds
+    (``steps`` back-to-back calls between two events per round), so that all of them see the
+    same clock and thermal state."""
+    import numpy as np
+    t = {n: [] for n in fns}
+    for _ in range(rounds):
+        for n, f in fns.items():
+            t[n].append(time_calls(torch, f, warmup, steps))
+    return {n: float(np.median(v)) for n, v in t.items()}
+
+
 def measure_layouts(args, fa, si, cm, torch, dec=None):
-    """The forward and the backward on layout variants: the prefill workload with the tensors in
-    [B][T][h][d] (strided views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the pages'
-    padding example; with ``dec`` = (workload, q, k, v) of the decode, also the decode on the same
-    KV cache stored as [B][Tk][h][d]."""
+    """The forward and the backward on layout variants, each timed in alternating rounds with
+    the contiguous [B][h][T][d] call on the same data: the prefill workload with the tensors in
+    [B][T][h][d] (strided views), and d_head = 80 with 20 heads (B=8, T=4096, causal), the
+    pages' padding example (reported against the true FLOPs and against the FLOPs of the
+    128-wide kernel that runs it); with ``dec`` = (workload, q, k, v) of the decode, also the
+    decode on the same KV cache stored as [B][Tk][h][d]."""
     import numpy as np
     peak = cm.MI355X_PEAK_BF16_DENSE_FLOPS / 1e12
-    K = args.extra_steps or 20
+    K = args.extra_steps or 10
     res = {}
-    for key, (B, h, T, d, strided) in {"bthd": (8, 32, 4096, 128, True),
-                                        "d80": (8, 20, 4096, 80, False)}.items():
-        wl = si.custom_workload(B, h, T, T, d, True, name=key)
-        q, k, v = si.make_inputs(wl, seed=0)
-        if strided:
-            def bthd(bits):
-                return upload(np.ascontiguousarray(bits.transpose(0, 2, 1, 3))).transpose(1, 2)
-            tq, tk, tv = bthd(q), bthd(k), bthd(v)
-            call = lambda: fa.fa_fwd_strided(tq, tk, tv, causal=True, scale=wl.scale)
-        else:
-            tq, tk, tv = upload(q), upload(k), upload(v)
-            o = torch.empty_like(tq)
-            lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
-            call = lambda: fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse)
-        del q, k, v
-        ms = time_calls(torch, call, 3, K)
-        flops = cm.attention_flops(B, h, T, T, d, True)
-        tf = flops / (ms * 1e-3) / 1e12
-        eprint(f"[bench] layout {key}: B={B} h={h} T={T} d={d} avg {ms:.4f} ms  {tf:.1f} TFLOP/s  "
-               f"{100 * tf / peak:.1f}% of {peak:.0f}")
-        res[key] = {"metric": f"attention fwd TFLOP/s, causal, d_head={d}" +
-                              (", [B][T][h][d] inputs" if strided else ", padded to 128 on chip"),
-                    "value": tf, "unit": "TFLOP/s", "steps": K, "warmup": 3, "avg_ms": ms,
-                    "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                                 "frac": tf / peak, "traffic": None},
+
+    def bthd(t):
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+    # forward: [B][T][h][d] against contiguous, same values
+    B, h, T, d = 8, 32, 4096, 128
+    wl = si.custom_workload(B, h, T, T, d, True, name="bthd")
+    q, k, v = si.make_inputs(wl, seed=0)
+    cq, ck, cv = upload(q), upload(k), upload(v)
+    del q, k, v
+    sq, sk, sv = bthd(cq), bthd(ck), bthd(cv)
+    co, so = torch.empty_like(cq), bthd(torch.empty_like(cq))
+    lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
+    ms = interleaved(torch, {
+        "contiguous": lambda: fa.fa_fwd(cq, ck, cv, causal=True, scale=wl.scale, o=co, lse=lse),
+        "bthd": lambda: fa.fa_fwd_strided(sq, sk, sv, causal=True, scale=wl.scale, o=so,
+                                          lse=lse)}, 3, K)
+    flops = cm.attention_flops(B, h, T, T, d, True)
+    tf = {n: flops / (m * 1e-3) / 1e12 for n, m in ms.items()}
+    eprint(f"[bench] layout bthd: B={B} h={h} T={T} d={d} {ms['bthd']:.4f} ms {tf['bthd']:.1f} "
+           f"TFLOP/s against contiguous {ms['contiguous']:.4f} ms {tf['contiguous']:.1f} "
+           f"(ratio {ms['bthd'] / ms['contiguous']:.3f})")
+    res["bthd"] = {"metric": "attention fwd TFLOP/s, causal, d_head=128, [B][T][h][d] q, k, v and o",
+                   "value": tf["bthd"], "unit": "TFLOP/s", "steps": K, "warmup": 3,
+                   "avg_ms": ms["bthd"], "contiguous_ms": ms["contiguous"],
+                   "time_ratio_vs_contiguous": ms["bthd"] / ms["contiguous"],
+                   "roofline": {"bound": "mfma", "achieved": tf["bthd"], "peak": peak,
+                                "unit": "TFLOP/s", "frac": tf["bthd"] / peak, "traffic": None},
+                   "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
+                              "layout": "BTHD strided", "flops": flops,
+                              "timing": "median of 5 rounds alternating with the contiguous call"}}
+
+    # backward on the same data: [B][T][h][d] tensors against contiguous
+    dob = si.make_grad(wl, seed=0)
+    cdo = upload(dob)
+    del dob
+    sdo = bthd(cdo)
+    fa.fa_fwd(cq, ck, cv, causal=True, scale=wl.scale, o=co, lse=lse)
+    fa.fa_fwd_strided(sq, sk, sv, causal=True, scale=wl.scale, o=so, lse=lse)
+    cg = [torch.empty_like(cq) for _ in range(3)]
+    sg = [bthd(torch.empty_like(cq)) for _ in range(3)]
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, h, T), dtype=torch.uint8, device="cuda")
+    ms = interleaved(torch, {
+        "contiguous": lambda: fa.fa_bwd(cq, ck, cv, co, cdo, lse, causal=True, scale=wl.scale,
+                                        dq=cg[0], dk=cg[1], dv=cg[2], workspace=ws),
+        "bthd": lambda: fa.fa_bwd_strided(sq, sk, sv, so, sdo, lse, causal=True, scale=wl.scale,
+                                          dq=sg[0], dk=sg[1], dv=sg[2], workspace=ws)},
+        2, max(3, K // 3))
+    bflops = cm.attention_bwd_flops(B, h, T, T, d, True)
+    tfb = {n: bflops / (m * 1e-3) / 1e12 for n, m in ms.items()}
+    eprint(f"[bench] layout bwd_bthd: {ms['bthd']:.4f} ms {tfb['bthd']:.1f} TFLOP/s (2.5x fwd "
+           f"FLOPs) against contiguous {ms['contiguous']:.4f} ms {tfb['contiguous']:.1f} "
+           f"(ratio {ms['bthd'] / ms['contiguous']:.3f})")
+    res["bwd_bthd"] = {"metric": "attention backward TFLOP/s (2.5x forward FLOPs), causal, "
+                                 "d_head=128, [B][T][h][d] tensors",
+                       "value": tfb["bthd"], "unit": "TFLOP/s", "steps": max(3, K // 3),
+                       "warmup": 2, "avg_ms": ms["bthd"], "contiguous_ms": ms["contiguous"],
+                       "time_ratio_vs_contiguous": ms["bthd"] / ms["contiguous"],
+                       "roofline": {"bound": "mfma", "achieved": tfb["bthd"], "peak": peak,
+                                    "unit": "TFLOP/s", "frac": tfb["bthd"] / peak,
+                                    "traffic": None},
+                       "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
+                                  "layout": "BTHD strided", "flops": bflops}}
+    del cq, ck, cv, sq, sk, sv, co, so, lse, cdo, sdo, cg, sg, ws
+    torch.cuda.empty_cache()
+
+    # d_head = 80 (20 heads), padded to 128 on chip: forward and backward
+    B, h, T, d = 8, 20, 4096, 80
+    wl = si.custom_workload(B, h, T, T, d, True, name="d80")
+    q, k, v = si.make_inputs(wl, seed=0)
+    dob = si.make_grad(wl, seed=0)
+    tq, tk, tv, tdo = upload(q), upload(k), upload(v), upload(dob)
+    del q, k, v, dob
+    o = torch.empty_like(tq)
+    lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
+    gr = [torch.empty_like(tq) for _ in range(3)]
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, h, T), dtype=torch.uint8, device="cuda")
+    fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse)
+    ms = interleaved(torch, {
+        "fwd": lambda: fa.fa_fwd(tq, tk, tv, causal=True, scale=wl.scale, o=o, lse=lse),
+        "bwd": lambda: fa.fa_bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=wl.scale,
+                                 dq=gr[0], dk=gr[1], dv=gr[2], workspace=ws)}, 2, max(3, K // 2))
+    for key, m, fl, padded, what in (
+            ("d80", ms["fwd"], cm.attention_flops(B, h, T, T, d, True),
+             cm.attention_flops(B, h, T, T, 128, True), "attention fwd"),
+            ("bwd_d80", ms["bwd"], cm.attention_bwd_flops(B, h, T, T, d, True),
+             cm.attention_bwd_flops(B, h, T, T, 128, True), "attention backward")):
+        tf_true = fl / (m * 1e-3) / 1e12
+        tf_pad = padded / (m * 1e-3) / 1e12
+        eprint(f"[bench] layout {key}: B={B} h={h} T={T} d={d} {m:.4f} ms  {tf_true:.1f} TFLOP/s "
+               f"of d=80 ({100 * tf_true / peak:.1f}%), {tf_pad:.1f} TFLOP/s of the 128-wide "
+               f"kernel's work ({100 * tf_pad / peak:.1f}%)")
+        res[key] = {"metric": f"{what} TFLOP/s, causal, d_head=80 (padded to 128 on chip)",
+                    "value": tf_true, "unit": "TFLOP/s", "avg_ms": m,
+                    "padded_tflops": tf_pad, "padded_frac": tf_pad / peak,
+                    "roofline": {"bound": "mfma", "achieved": tf_true, "peak": peak,
+                                 "unit": "TFLOP/s", "frac": tf_true / peak, "traffic": None},
                     "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
-                               "layout": "BTHD strided" if strided else "BHTD contiguous",
-                               "flops": flops}}
-        del tq, tk, tv
-        torch.cuda.empty_cache()
-    # the backward on the same variants (fa_bwd_strided): [B][T][h][d] inputs and outputs at the
-    # prefill shape, and d_head = 80 contiguous (padded on chip)
-    for key, (B, h, T, d, strided) in {"bwd_bthd": (8, 32, 4096, 128, True),
-                                        "bwd_d80": (8, 20, 4096, 80, False)}.items():
-        wl = si.custom_workload(B, h, T, T, d, True, name=key)
-        q, k, v = si.make_inputs(wl, seed=0)
-        dob = si.make_grad(wl, seed=0)
-        if strided:
-            def lay(bits):
-                return upload(np.ascontiguousarray(bits.transpose(0, 2, 1, 3))).transpose(1, 2)
-        else:
-            lay = upload
-        tq, tk, tv, tdo = lay(q), lay(k), lay(v), lay(dob)
-        del q, k, v, dob
-        to = torch.empty_like(tq)
-        lse = torch.empty((B, h, T), dtype=torch.float32, device="cuda")
-        fa.fa_fwd_strided(tq, tk, tv, causal=True, scale=wl.scale, o=to, lse=lse)
-        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-        ws = torch.empty(fa.fa_bwd_workspace_size(B, h, T), dtype=torch.uint8, device="cuda")
-        call = lambda: fa.fa_bwd_strided(tq, tk, tv, to, tdo, lse, causal=True, scale=wl.scale,
-                                         dq=dq, dk=dk, dv=dv, workspace=ws)
-        ms = time_calls(torch, call, 3, max(5, K // 4))
-        flops = cm.attention_bwd_flops(B, h, T, T, d, True)
-        tf = flops / (ms * 1e-3) / 1e12
-        eprint(f"[bench] layout {key}: B={B} h={h} T={T} d={d} avg {ms:.4f} ms  {tf:.1f} TFLOP/s "
-               f"(2.5x fwd FLOPs)  {100 * tf / peak:.1f}% of {peak:.0f}")
-        res[key] = {"metric": f"attention backward TFLOP/s (2.5x forward FLOPs), causal, "
-                              f"d_head={d}" + (", [B][T][h][d] tensors" if strided else
-                                               ", padded to 128 on chip"),
-                    "value": tf, "unit": "TFLOP/s", "steps": max(5, K // 4), "warmup": 3,
-                    "avg_ms": ms,
-                    "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                                 "frac": tf / peak, "traffic": None},
-                    "config": {"B": B, "h": h, "T": T, "d_head": d, "causal": True,
-                               "layout": "BTHD strided" if strided else "BHTD contiguous",
-                               "flops": flops}}
-        del tq, tk, tv, tdo, to, lse, dq, dk, dv, ws
-        torch.cuda.empty_cache()
+                               "flops": fl, "padded_flops": padded}}
+    del tq, tk, tv, tdo, o, lse, gr, ws
+    torch.cuda.empty_cache()
+
     if dec is not None:
         wd, dq_, dk_, dv_ = dec
         kc = dk_.transpose(1, 2).contiguous().transpose(1, 2)   # [B][Tk][h][d] storage
@@ -597,19 +647,26 @@ def measure_layouts(args, fa, si, cm, torch, dec=None):
         lse = torch.empty((wd.B, wd.h), dtype=torch.float32, device="cuda")
         ws = torch.empty(fa.fa_decode_workspace_size(wd.B, wd.h, wd.d, wd.num_splits),
                          dtype=torch.uint8, device="cuda")
-        call = lambda: fa.fa_decode_strided(dq_, kc, vc, num_splits=wd.num_splits, scale=wd.scale,
-                                            o=o, lse=lse, workspace=ws)
-        ms = time_calls(torch, call, 3, K)
+        ms = interleaved(torch, {
+            "contiguous": lambda: fa.fa_decode(dq_, dk_, dv_, num_splits=wd.num_splits,
+                                               scale=wd.scale, o=o, lse=lse, workspace=ws),
+            "bthd": lambda: fa.fa_decode_strided(dq_, kc, vc, num_splits=wd.num_splits,
+                                                 scale=wd.scale, o=o, lse=lse, workspace=ws)},
+            3, K)
         kv = wd.B * wd.h * wd.Tk * cm.decode_kv_bytes_per_token(wd.d)
-        gbs = kv / (ms * 1e-3) / 1e9
+        gbs = {n: kv / (m * 1e-3) / 1e9 for n, m in ms.items()}
         hbm = cm.MI355X_PEAK_HBM_BYTES_PER_S / 1e9
         eprint(f"[bench] layout decode_bthd: B={wd.B} h={wd.h} Tk={wd.Tk} d={wd.d} "
-               f"S={wd.num_splits} avg {ms:.4f} ms  {gbs:.0f} GB/s  {100 * gbs / hbm:.1f}%")
+               f"S={wd.num_splits} {ms['bthd']:.4f} ms {gbs['bthd']:.0f} GB/s "
+               f"({100 * gbs['bthd'] / hbm:.1f}%) against contiguous {gbs['contiguous']:.0f} "
+               f"(ratio {ms['bthd'] / ms['contiguous']:.3f})")
         res["decode_bthd"] = {
             "metric": "decode HBM GB/s (K+V bytes / split+combine time), KV cache in [B][Tk][h][d]",
-            "value": gbs, "unit": "GB/s", "steps": K, "warmup": 3, "avg_ms": ms,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": hbm, "unit": "GB/s",
-                         "frac": gbs / hbm, "traffic": None},
+            "value": gbs["bthd"], "unit": "GB/s", "steps": K, "warmup": 3,
+            "avg_ms": ms["bthd"], "contiguous_ms": ms["contiguous"],
+            "time_ratio_vs_contiguous": ms["bthd"] / ms["contiguous"],
+            "roofline": {"bound": "hbm", "achieved": gbs["bthd"], "peak": hbm, "unit": "GB/s",
+                         "frac": gbs["bthd"] / hbm, "traffic": None},
             "config": {"B": wd.B, "h": wd.h, "Tk": wd.Tk, "d_head": wd.d,
                        "num_splits": wd.num_splits, "layout": "BTHD strided KV cache"}}
         del kc, vc, o, lse, ws

@@ -543,6 +543,11 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < PRE; ++i) ring[i] = v_opnd(v_at(st), i);
       }
+      // After the item's last S^T section the Q fragment is free: the next item's Q rows are
+      // requested here, a whole step before its first S^T section needs them.  (They follow
+      // the request of the next item's tile 1 and precede this item's output stores, the order
+      // the waits below count on.)
+      if (t == ntiles - 1 && has_nxt) load_q(nxt);
       __syncthreads();
     };
 
@@ -559,7 +564,6 @@ void fa_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_s_setprio(1);
     if (active(ntiles - 1))
       section(ValuesOnly{}, 0u, v_at((g0 + ntiles - 1) & (kStages - 1)));
-    if (has_nxt) load_q(nxt);   // the S^T fragment is free from here on
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     // O = acc / l16, LSE = (m + log2 l) * ln 2 (touches only this wave's output staging)
