@@ -748,7 +748,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "softmax", "elementwise",
-                                       "layouts"],
+                                       "layouts", "configs"],
                     default=None,
                     help="run one half of the step (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -814,6 +814,18 @@ def main():
                "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                "roofline": sm["roofline"], "config": {"workload": "softmax_rows_4096x4096_f32"},
                "cpu_baseline": sm.get("cpu_baseline")}
+        print(json.dumps(out), flush=True)
+        return
+
+    if args.only == "configs":
+        cf = measure_configs(args, fa, si, cm, torch)
+        c4 = cf["C4"]
+        out = {"metric": c4["metric"], "value": c4["value"], "unit": c4["unit"], "n_gpus": 1,
+               "steps": c4["timing"]["trials"], "warmup": 3, "ms_per_step": c4["timing"]["avg_ms"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic", "roofline": c4["roofline"],
+               "config": {"workload": "longctx_causal_b2_h32_t16384_d128_keyspikes"},
+               "cpu_baseline": c4.get("cpu_baseline"), "configs": cf}
         print(json.dumps(out), flush=True)
         return
 
