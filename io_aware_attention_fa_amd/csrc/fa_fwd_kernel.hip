@@ -308,10 +308,10 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * g;
-      u32x4_t w = buf_load16(
-          rq, col < dd ? ((uint32_t)qrow * q_t + (uint32_t)col) * 2u : kPadOffset);
-      w ^= p.q_sign;
-      qf[s] = as_bf16x8(w);
+      // (the loaded value is not touched here: the loads stay in flight until the item's first
+      // matrix section, which applies the sign of a negative scale)
+      qf[s] = as_bf16x8(buf_load16(
+          rq, col < dd ? ((uint32_t)qrow * q_t + (uint32_t)col) * 2u : kPadOffset));
     }
   };
   // one K/V tile of an item into stage st
@@ -459,12 +459,23 @@ void fa_fwd_kernel(FwdParams p) {
       }
     };
 
-    auto step = [&](const int t, auto mode) {
+    // q_next: this is the item's last score step (t = ntiles - 1, ntiles > 1); it requests the
+    // next item's Q rows.  It is a separate instantiation, outside the loop over the other
+    // steps, so that no step in that loop has Q loads in flight into the fragment it reads.
+    auto step = [&](const int t, auto mode, auto q_next) {
       constexpr int MODE = decltype(mode)::value;
       const int st = (g0 + t) & (kStages - 1), st_prev = (g0 + t + kStages - 1) & (kStages - 1);
       // ================= matrix section =================
       __builtin_amdgcn_s_setprio(1);
       request(t + 2);
+      if (MODE == kSecScores) {
+        // the item's Q rows are needed from here on: negate them for a negative scale (exact)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8_t x = qf[s];
+          qf[s] = as_bf16x8(__builtin_bit_cast(u32x4_t, x) ^ p.q_sign);
+        }
+      }
       // A wave's tiles form a prefix (causal skipping is monotone in t), so after step 0 a wave
       // that has the previous tile's P^T to apply runs both products; at the step after its
       // last tile the S^T product is wasted (and ignored), which keeps a single code path for
@@ -547,7 +558,9 @@ void fa_fwd_kernel(FwdParams p) {
       // requested here, a whole step before its first S^T section needs them.  (They follow
       // the request of the next item's tile 1 and precede this item's output stores, the order
       // the waits below count on.)
-      if (t == ntiles - 1 && has_nxt) load_q(nxt);
+      if constexpr (decltype(q_next)::value) {
+        if (has_nxt) load_q(nxt);
+      }
       __syncthreads();
     };
 
@@ -557,13 +570,18 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < kRing; ++i) ring[i] = k_opnd(ks0, i);
     }
-    step(0, ScoresOnly{});
-    for (int t = 1; t < ntiles; ++t) step(t, Both{});
+    using NoQ = std::false_type;
+    using WithQ = std::true_type;
+    step(0, ScoresOnly{}, NoQ{});
+    for (int t = 1; t < ntiles - 1; ++t) step(t, Both{}, NoQ{});
+    if (ntiles > 1) step(ntiles - 1, Both{}, WithQ{});
 
     // ---- last step: the last tile's P^T, then the epilogue in the vector slot ----
     __builtin_amdgcn_s_setprio(1);
     if (active(ntiles - 1))
       section(ValuesOnly{}, 0u, v_at((g0 + ntiles - 1) & (kStages - 1)));
+    // (an item with a single tile, Tk <= 64 only: its Q request comes after the P^T section)
+    if (ntiles == 1 && has_nxt) load_q(nxt);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     // O = acc / l16, LSE = (m + log2 l) * ln 2 (touches only this wave's output staging)
@@ -584,14 +602,18 @@ void fa_fwd_kernel(FwdParams p) {
               *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.o) + orow + col) = f;
           }
       }
-    } else if (wave_has_rows) {
+    } else {
       // In the MFMA layout a lane holds 8-byte pieces of one row; the rows go through this
       // wave's 4 KB of LDS, 64 columns at a time (16-byte chunks XOR-swizzled by row), so that
-      // each global store writes whole 128-byte row segments.
+      // each store writes whole 128-byte row segments.  The stores are buffer stores that every
+      // wave issues, rows past Tq (or every row of a wave without rows) and padding columns at
+      // an offset past the buffer's range, which the hardware drops: with no branch around them
+      // the compiler counts them in every path, so the next item's first score product waits
+      // only for its Q rows, not for these stores.
       const uint32_t ob = (uint32_t)reinterpret_cast<uintptr_t>(ostage) + (uint32_t)wave * 4096u;
-      const int rows = p.Tq - qw0;   // valid rows of this wave (>= 1)
-      uint16_t* const obase = static_cast<uint16_t*>(p.o) + head_off(cur.bh, p.o_b, p.o_h, p.Tq) +
-                              (int64_t)qw0 * o_t;
+      const int rows = p.Tq - qw0;   // valid rows of this wave (<= 0: none)
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+          static_cast<uint16_t*>(p.o) + head_off(cur.bh, p.o_b, p.o_h, p.Tq), range(p.Tq, o_t));
 #pragma unroll
       for (int h = 0; h < ND / 2; ++h) {
 #pragma unroll
@@ -608,13 +630,23 @@ void fa_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int row = 8 * i + (lane >> 3), ch = lane & 7;
           const u32x4_t w = lds_read16u(ob + row * 128u + 16u * (ch ^ (row & 7)));
-          if (row < rows && 64 * h + 8 * ch < dd)
-            *reinterpret_cast<u32x4_t*>(obase + (int64_t)row * o_t + 64 * h + 8 * ch) = w;
+          const uint32_t off =
+              row < rows && 64 * h + 8 * ch < dd
+                  ? ((uint32_t)(qw0 + row) * o_t + (uint32_t)(64 * h + 8 * ch)) * 2u
+                  : kPadOffset;
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
         }
       }
     }
-    if (wave_has_rows && qrow < p.Tq && g == 0)
-      p.lse[(size_t)cur.bh * p.Tq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+    {
+      // LSE, one lane per row (the lanes of the other half hold the same rows)
+      const __amdgpu_buffer_rsrc_t rl =
+          make_rsrc(p.lse + (size_t)cur.bh * p.Tq, (uint32_t)p.Tq * 4u);
+      const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+      const uint32_t off = wave_has_rows && qrow < p.Tq && g == 0 ? (uint32_t)qrow * 4u
+                                                                  : kPadOffset;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), rl, off, 0, 0);
+    }
     __syncthreads();
 
     g0 += ntiles;

@@ -278,3 +278,24 @@ def test_rejected_call_leaves_device_outputs_untouched(gpu):
     assert e.value.status == gpu.FA_ERR_CAUSAL_TQ_GT_TK
     torch.cuda.synchronize()
     assert torch.all(o == 3.0) and torch.all(lse == 7.0)
+
+
+@pytest.mark.parametrize("d,causal,scale", [(128, True, -0.0883883), (64, False, -0.3),
+                                           (128, False, 0.0), (64, True, -2.5)])
+def test_negative_and_zero_scales(gpu, d, causal, scale):
+    """A negative scale is applied on chip by negating Q (exact); zero gives uniform attention."""
+    wl = si.custom_workload(2, 3, 300, 300, d, causal)
+    q, k, v = si.make_inputs(wl, seed=17, threads=4)
+    res = run_fwd(gpu, q, k, v, causal, scale)
+    assert_bf16_is_rne_of_f32(res)
+    heads = {(b, hh): np.arange(300) for b in range(2) for hh in range(3)}
+    refs = {bh: ref.naive_attention_head(si.bf16_bits_to_f64(q[bh]), si.bf16_bits_to_f64(k[bh]),
+                                         si.bf16_bits_to_f64(v[bh]), scale, causal)
+            for bh in heads}
+    o32 = res["o32"].cpu().numpy()
+    l32 = res["lse32"].cpu().numpy()
+    for bh in heads:
+        d_o = float(np.max(np.abs(o32[bh] - refs[bh][0])))
+        d_l = float(np.max(np.abs(l32[bh] - refs[bh][1])))
+        assert d_o <= O_TOL and d_l <= LSE_TOL, (bh, d_o, d_l)
+    log(f"[parity] scale={scale} d={d} causal={causal}: ok")
