@@ -226,6 +226,39 @@ __device__ __forceinline__ void block_of(const BwdParams& p, bool reverse, int& 
   blk = __builtin_amdgcn_readfirstlane(reverse ? p.nblk - 1 - j : j);
 }
 
+// Persistent schedule of the dK/dV kernel: at most one workgroup per CU, each running several
+// (head, key block) items one after the other, so that a CU starts its next block without a new
+// workgroup's dispatch (which cost about as much as 15-20 of its pipeline steps).  Blocks are
+// paired as (nblk - 1 - j, j): under the causal mask block j sees Tq - 128 j queries, so the costs
+// of a pair add up to the same total for every j and dealing pairs round-robin balances the CUs.
+// With groups == 8 workgroup n belongs to group n % 8 (the XCD it is dispatched to) and takes the
+// pairs of heads n % 8, n % 8 + 8, ..., so the tiles a head streams are shared in that XCD's L2.
+// body(bh, blk, tid) runs one item with tid, the thread index, rebuilt per item from the wave
+// index (a scalar) and the lane's position in the wave and passed through an opaque copy: every
+// lane-dependent value of an item is then computed inside it, so the compiler neither hoists such
+// values out of the item loop nor keeps them live across an item (the kernel's steady state
+// fills the registers).  The barrier between items lets the next item's loads reuse the LDS.
+template <class F>
+__device__ __forceinline__ void for_each_block(const BwdParams& p, F&& body) {
+  const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int u = 0;; ++u) {
+    const int X = p.groups, n = blockIdx.x;
+    const int x = n % X, c = n / X;
+    const int C = ((int)gridDim.x - x + X - 1) / X;   // workgroups of group x
+    const int np = (p.nblk + 1) / 2;                   // block pairs per head
+    const int PX = ((p.BH - x + X - 1) / X) * np;      // pairs of group x
+    const int pp = c + (u >> 1) * C;
+    if (pp >= PX) break;
+    const int hl = pp / np, j = pp - hl * np;
+    const int blk = (u & 1) ? j : p.nblk - 1 - j;
+    if ((u & 1) && blk == p.nblk - 1 - j) continue;   // the middle block of an odd count
+    if (u > 0) __syncthreads();
+    int tid = wave0 * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(tid));
+    body(__builtin_amdgcn_readfirstlane(x + X * hl), __builtin_amdgcn_readfirstlane(blk), tid);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Preprocess: -D_i = -<dO_i, O_i> (fp32 sum of bf16 products) and LSE_i * log2(e).
 // One row per D/8 lanes (16 bytes each); rows = B * h * Tq.
@@ -386,292 +419,297 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
   __shared__ __attribute__((aligned(1024))) float lds_p[4 * 2 * PF / 4];
   __shared__ __attribute__((aligned(256))) float lds_ld[2 * NST * LDS_LD];
+  for_each_block(p, [&](const int bh, const int blk, const int tid) {
   const uint32_t lq = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t ldo = lq + NST * T::BYTES;
-  const uint32_t ll = (uint32_t)reinterpret_cast<uintptr_t>(lds_ld);
-  const uint32_t ld = ll + NST * LDS_LD * 4;
+    const uint32_t ll = (uint32_t)reinterpret_cast<uintptr_t>(lds_ld);
+    const uint32_t ld = ll + NST * LDS_LD * 4;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pr = wave & 3;     // wave pair
-  const bool role_k = wave < 4;
-  const int g = lane >> 5;
-  const Lanes<D, R, SPLIT ? 4 : kWavesK> ln(SPLIT ? pr : wave, lane);
-  // this lane's slot of the pair's P buffers (parity and part add immediates)
-  const uint32_t pfb =
-      (uint32_t)reinterpret_cast<uintptr_t>(lds_p) + (uint32_t)pr * (2 * PF) + 16u * lane;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pr = wave & 3;     // wave pair
+    const bool role_k = wave < 4;
+    const int g = lane >> 5;
+    const Lanes<D, R, SPLIT ? 4 : kWavesK> ln(SPLIT ? pr : wave, lane);
+    // this lane's slot of the pair's P buffers (parity and part add immediates)
+    const uint32_t pfb =
+        (uint32_t)reinterpret_cast<uintptr_t>(lds_p) + (uint32_t)pr * (2 * PF) + 16u * lane;
 
-  int bh, blk;
-  block_of(p, false, bh, blk);
-  const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
-  const int key = blk * kOwnK + pr * 32 + (lane & 31);
+    const int off = p.Tk - p.Tq;   // query i sits at key position i + off (causal)
+    const int key = blk * kOwnK + pr * 32 + (lane & 31);
 
-  // query tiles this block needs: from the first query that sees its first key
-  const int nqt = (p.Tq + R - 1) / R;
-  const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwnK - off) / R) : 0;
-  const int nt = nqt - t0;
+    // query tiles this block needs: from the first query that sees its first key
+    const int nqt = (p.Tq + R - 1) / R;
+    const int t0 = CAUSAL ? __builtin_amdgcn_readfirstlane(max(0, blk * kOwnK - off) / R) : 0;
+    const int nt = nqt - t0;
 
-  const int hd = GEN ? p.d : D;   // true head dim
-  const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
-  const u32x4_t rq = rsrc_words(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
-                                head_bytes(p.Tq, st_q, hd));
-  const u32x4_t rdo = rsrc_words(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
-                                 head_bytes(p.Tq, st_do, hd));
-  uint32_t gq[T::LPW], gdo[T::LPW];   // this wave's global load offsets within a tile
-#pragma unroll
-  for (int i = 0; i < T::LPW; ++i) {
-    gq[i] = ln.goff(i, st_q, hd);
-    gdo[i] = ln.goff(i, st_do, hd);
-  }
-  // role K stages L2 (for P), role V stages -D (the dP seed); four identical copies each
-  const u32x4_t rld = role_k ? rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u)
-                             : rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
-  const uint32_t lld = role_k ? ll : ld;
-  auto request = [&](int it) {   // tile t0 + it into stage it % NST
-    const int st = it % NST;
-    const uint32_t g0q = (uint32_t)(t0 + it) * (R * 2u) * st_q;
-    const uint32_t g0d = (uint32_t)(t0 + it) * (R * 2u) * st_do;
-#pragma unroll
+    const int hd = GEN ? p.d : D;   // true head dim
+    const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
+    const u32x4_t rq = rsrc_words(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
+                                  head_bytes(p.Tq, st_q, hd));
+    const u32x4_t rdo = rsrc_words(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
+                                   head_bytes(p.Tq, st_do, hd));
+    uint32_t gq[T::LPW], gdo[T::LPW];   // this wave's global load offsets within a tile
+  #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
-      if (SPLIT) {
-        lds_dma16(role_k ? rq : rdo, (role_k ? lq : ldo) + st * T::BYTES + ln.dma_l[i],
-                  role_k ? g0q + gq[i] : g0d + gdo[i]);
-      } else {
-        lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0q + gq[i]);
-        lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0d + gdo[i]);
-      }
+      gq[i] = ln.goff(i, st_q, hd);
+      gdo[i] = ln.goff(i, st_do, hd);
     }
-    // 64 values from the tile's first row on (the tile uses the first 32)
-    lds_dma4(rld, lld + st * (LDS_LD * 4), (uint32_t)((t0 + it) * R + lane) * 4u);
-  };
-  constexpr int PER = (SPLIT ? 1 : 2) * T::LPW + 1;   // vector-memory operations per tile
-
-  // K (role K) or V (role V) rows of this lane's key as B operands (k = 8 columns per half).
-  bf16x8_t kvf[NS];
-  {
-    const uint16_t* src = role_k ? p.k : p.v;
-    const Lay& lkv = role_k ? p.lk : p.lv;
-    const uint32_t st = row_stride<D, GEN>(lkv);
-    const __amdgpu_buffer_rsrc_t rkv =
-        make_rsrc(src + head_elem<D, GEN>(p, lkv, bh, p.Tk), head_bytes(p.Tk, st, hd));
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kvf[s] = as_bf16x8(buf_load16(rkv, off16(key, 16 * s + 8 * g, st, hd)));
-  }
-
-  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
-  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and the K/V rows)
-  __syncthreads();
-
-  f32x16_t acc[ND];   // dV^T (role K) or dK^T (role V)
-#pragma unroll
-  for (int db = 0; db < ND; ++db) acc[db] = f32x16_t{};
-  bf16x8_t ring[kRing];
-  const Region<D> rQ(lq, ln.row_off, ln.tr_off), rO(ldo, ln.row_off, ln.tr_off);
-
-  if (role_k) {
-    // ------------------------------- role K -------------------------------
-    // P is zeroed for queries below thr: keys past the end see nothing; causal keys see
-    // queries from key - off on.  thr4: thr relative to the first query this lane holds.
-    const int thr4 = key >= p.Tk ? (1 << 30) : (CAUSAL ? key - off - 4 * g : -(1 << 30));
-    // Tiles from s_free on need no mask (wave-uniform): no key of this wave is past the end,
-    // and the tile starts at or below the diagonal of this wave's last key.
-    const int kw0 = blk * kOwnK + pr * 32;
-    int s_free = 0;
-    if (kw0 + 31 >= p.Tk) {
-      s_free = INT32_MAX;
-    } else if (CAUSAL) {
-      const int x = kw0 + 31 - off;   // the first query that sees every key of this wave
-      s_free = x <= 0 ? 0 : (x + R - 1) / R - t0;
-    }
-    f32x16_t sacc;         // S of the next tile (32 queries x this key)
-    bf16x8_t pb[2][2];     // [tile parity][k-step]: P as C-part operands
-    auto step = [&](auto parts, auto stage, int s) {
-      using PT = decltype(parts);
-      constexpr int ST = decltype(stage)::value;
-      constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-      constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-      // vector instructions per C-part MFMA: about 4.5 per score with the mask, 2.5 without
-      constexpr int VPM = PT::m ? 9 : 5;
-      using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 4 : 0, PT::c, next, kRing>;
-      constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
-      constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
-      constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
-      constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // parities (NST is even)
-      asm volatile("" : "+s"(s));
-      if (s + AHEAD < nt) request(s + AHEAD);
-      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rO.tr_opnd(so, i % ND, i / ND); };
-      auto opnd = [&](int i) -> bf16x8_t {
-        if (i < nc) return c_opnd(so_c, i);
-        return rQ.row_opnd(so_a, 0, i - nc);
-      };
-      if constexpr (!PT::c) {
-#pragma unroll
-        for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
-      }
-      if constexpr (PT::v) {
-        f32x4_t L4[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
-        const int lt = thr4 - (t0 + s) * R;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int a = i >> 2, e = i & 3;
-          float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
-          if (PT::m && 8 * a + e < lt) pv = 0.f;
-          sacc[i] = pv;
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          lds_write_f32x4(pfb + PV * PF + 1024u * a,
-                          f32x4_t{sacc[4 * a], sacc[4 * a + 1], sacc[4 * a + 2], sacc[4 * a + 3]});
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pb[PV][ks] = pack_kstep(sacc, ks);
-      }
-#pragma unroll
-      for (int i = 0; i < S::n; ++i) {
-        const bf16x8_t a = ring[i % kRing];
-        if (i + kRing < S::n)
-          ring[i % kRing] = opnd(i + kRing);
-        else if (next)
-          ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
-        if (i < nc) {
-          acc[i % ND] = mfma_32x32x16(a, pb[PC][i / ND], acc[i % ND]);
+    // role K stages L2 (for P), role V stages -D (the dP seed); four identical copies each
+    const u32x4_t rld = role_k ? rsrc_words(p.l2 + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u)
+                               : rsrc_words(p.dd + (size_t)bh * (size_t)p.Tq, (uint32_t)p.Tq * 4u);
+    const uint32_t lld = role_k ? ll : ld;
+    auto request = [&](int it) {   // tile t0 + it into stage it % NST
+      const int st = it % NST;
+      const uint32_t g0q = (uint32_t)(t0 + it) * (R * 2u) * st_q;
+      const uint32_t g0d = (uint32_t)(t0 + it) * (R * 2u) * st_do;
+  #pragma unroll
+      for (int i = 0; i < T::LPW; ++i) {
+        if (SPLIT) {
+          lds_dma16(role_k ? rq : rdo, (role_k ? lq : ldo) + st * T::BYTES + ln.dma_l[i],
+                    role_k ? g0q + gq[i] : g0d + gdo[i]);
         } else {
-          const int j = i - nc;
-          sacc = mfma_32x32x16(a, kvf[j], j == 0 ? f32x16_t{} : sacc);
+          lds_dma16(rq, lq + st * T::BYTES + ln.dma_l[i], g0q + gq[i]);
+          lds_dma16(rdo, ldo + st * T::BYTES + ln.dma_l[i], g0d + gdo[i]);
         }
       }
-      sched_pattern<S>();
-      // the next step reads tile s + 2 (role K's S)
-      wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
-      __syncthreads();
+      // 64 values from the tile's first row on (the tile uses the first 32)
+      lds_dma4(rld, lld + st * (LDS_LD * 4), (uint32_t)((t0 + it) * R + lane) * 4u);
     };
-    step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
-    step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+    constexpr int PER = (SPLIT ? 1 : 2) * T::LPW + 1;   // vector-memory operations per tile
+
+    // K (role K) or V (role V) rows of this lane's key as B operands (k = 8 columns per half).
+    bf16x8_t kvf[NS];
     {
-      // steps 1 .. nt: whole chains of the NST stage variants with the mask while a chain may
-      // hold a tile that needs it, then chains without (each chain left after step nt)
-      int s = 1;
-      auto chain = [&](auto parts) {
-        step(parts, Stage<1>{}, s); if (++s > nt) return true;
-        step(parts, Stage<2>{}, s); if (++s > nt) return true;
-        step(parts, Stage<3>{}, s); if (++s > nt) return true;
-        step(parts, Stage<4>{}, s); if (++s > nt) return true;
-        step(parts, Stage<5>{}, s); if (++s > nt) return true;
-        step(parts, Stage<0>{}, s); if (++s > nt) return true;
-        return false;
-      };
-      bool fin = false;
-      while (!fin && s < s_free) fin = chain(Parts<true, true, true, true>{});
-      while (!fin) fin = chain(Parts<true, true, true, false>{});
+      const uint16_t* src = role_k ? p.k : p.v;
+      const Lay& lkv = role_k ? p.lk : p.lv;
+      const uint32_t st = row_stride<D, GEN>(lkv);
+      const __amdgpu_buffer_rsrc_t rkv =
+          make_rsrc(src + head_elem<D, GEN>(p, lkv, bh, p.Tk), head_bytes(p.Tk, st, hd));
+  #pragma unroll
+      for (int s = 0; s < NS; ++s)
+        kvf[s] = as_bf16x8(buf_load16(rkv, off16(key, 16 * s + 8 * g, st, hd)));
     }
-    step(Parts<false, false, false, false>{}, Stage<0>{}, nt + 1);   // role V's last step
-  } else {
-    // ------------------------------- role V -------------------------------
-    // (fewer live registers than role K: a deeper operand ring at d = 128)
-    constexpr int kRingV = D == 128 ? 8 : kRing;
-    bf16x8_t ringv[kRingV];
-    f32x16_t dpacc;        // dP - D of tile s (kept for the dS of the next step)
-    bf16x8_t dsb[2][2];    // [tile parity][k-step]: dS as C-part operands
-    constexpr int VPM = 3;   // vector instructions per C-part MFMA (1.5 per score)
-    auto step = [&](auto parts, auto stage, int s) {
-      using PT = decltype(parts);
-      constexpr int ST = decltype(stage)::value;
-      constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-      constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-      using S = StepSeq<nc, na, PT::v ? VPM : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next,
-                        kRingV>;
-      constexpr uint32_t so_c = ((ST + NST - 2) % NST) * T::BYTES;   // tile s - 2
-      constexpr uint32_t so_n = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
-      constexpr uint32_t so_a = ST * T::BYTES;                       // tile s
-      constexpr int PC = ST & 1, PV = (ST + 1) & 1;   // parities of tiles s - 2 and s - 1
-      asm volatile("" : "+s"(s));
-      if (s + AHEAD < nt) request(s + AHEAD);
-      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rQ.tr_opnd(so, i % ND, i / ND); };
-      auto opnd = [&](int i) -> bf16x8_t {
-        if (i < nc) return c_opnd(so_c, i);
-        return rO.row_opnd(so_a, 0, i - nc);
+
+    for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
+    wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));   // tiles 0 and 1 (and the K/V rows)
+    __syncthreads();
+
+    f32x16_t acc[ND];   // dV^T (role K) or dK^T (role V)
+  #pragma unroll
+    for (int db = 0; db < ND; ++db) acc[db] = f32x16_t{};
+    bf16x8_t ring[kRing];
+    const Region<D> rQ(lq, ln.row_off, ln.tr_off), rO(ldo, ln.row_off, ln.tr_off);
+
+    if (role_k) {
+      // ------------------------------- role K -------------------------------
+      // P is zeroed for queries below thr: keys past the end see nothing; causal keys see
+      // queries from key - off on.  thr4: thr relative to the first query this lane holds.
+      const int thr4 = key >= p.Tk ? (1 << 30) : (CAUSAL ? key - off - 4 * g : -(1 << 30));
+      // Tiles from s_free on need no mask (wave-uniform): no key of this wave is past the end,
+      // and the tile starts at or below the diagonal of this wave's last key.
+      const int kw0 = blk * kOwnK + pr * 32;
+      int s_free = 0;
+      if (kw0 + 31 >= p.Tk) {
+        s_free = INT32_MAX;
+      } else if (CAUSAL) {
+        const int x = kw0 + 31 - off;   // the first query that sees every key of this wave
+        s_free = x <= 0 ? 0 : (x + R - 1) / R - t0;
+      }
+      f32x16_t sacc;         // S of the next tile (32 queries x this key)
+      bf16x8_t pb[2][2];     // [tile parity][k-step]: P as C-part operands
+      auto step = [&](auto parts, auto stage, int s) {
+        using PT = decltype(parts);
+        constexpr int ST = decltype(stage)::value;
+        constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+        constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+        // vector instructions per C-part MFMA: about 4.5 per score with the mask, 2.5 without
+        constexpr int VPM = PT::m ? 9 : 5;
+        using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 4 : 0, PT::c, next, kRing>;
+        constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+        constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
+        constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
+        constexpr int PC = (ST + 1) & 1, PV = ST & 1;                  // parities (NST is even)
+        asm volatile("" : "+s"(s));
+        if (s + AHEAD < nt) request(s + AHEAD);
+        auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t {
+          return rO.tr_opnd(so, i % ND, i / ND);
+        };
+        auto opnd = [&](int i) -> bf16x8_t {
+          if (i < nc) return c_opnd(so_c, i);
+          return rQ.row_opnd(so_a, 0, i - nc);
+        };
+        if constexpr (!PT::c) {
+  #pragma unroll
+          for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+        }
+        if constexpr (PT::v) {
+          f32x4_t L4[4];
+  #pragma unroll
+          for (int a = 0; a < 4; ++a)
+            L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
+          const int lt = thr4 - (t0 + s) * R;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int a = i >> 2, e = i & 3;
+            float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
+            if (PT::m && 8 * a + e < lt) pv = 0.f;
+            sacc[i] = pv;
+          }
+  #pragma unroll
+          for (int a = 0; a < 4; ++a)
+            lds_write_f32x4(pfb + PV * PF + 1024u * a,
+                            f32x4_t{sacc[4 * a], sacc[4 * a + 1], sacc[4 * a + 2],
+                                    sacc[4 * a + 3]});
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) pb[PV][ks] = pack_kstep(sacc, ks);
+        }
+  #pragma unroll
+        for (int i = 0; i < S::n; ++i) {
+          const bf16x8_t a = ring[i % kRing];
+          if (i + kRing < S::n)
+            ring[i % kRing] = opnd(i + kRing);
+          else if (next)
+            ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
+          if (i < nc) {
+            acc[i % ND] = mfma_32x32x16(a, pb[PC][i / ND], acc[i % ND]);
+          } else {
+            const int j = i - nc;
+            sacc = mfma_32x32x16(a, kvf[j], j == 0 ? f32x16_t{} : sacc);
+          }
+        }
+        sched_pattern<S>();
+        // the next step reads tile s + 2 (role K's S)
+        wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
+        __syncthreads();
       };
-      if constexpr (!PT::c) {
-#pragma unroll
-        for (int i = 0; i < kRingV && i < S::n; ++i) ringv[i] = opnd(i);
+      step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
+      step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+      {
+        // steps 1 .. nt: whole chains of the NST stage variants with the mask while a chain may
+        // hold a tile that needs it, then chains without (each chain left after step nt)
+        int s = 1;
+        auto chain = [&](auto parts) {
+          step(parts, Stage<1>{}, s); if (++s > nt) return true;
+          step(parts, Stage<2>{}, s); if (++s > nt) return true;
+          step(parts, Stage<3>{}, s); if (++s > nt) return true;
+          step(parts, Stage<4>{}, s); if (++s > nt) return true;
+          step(parts, Stage<5>{}, s); if (++s > nt) return true;
+          step(parts, Stage<0>{}, s); if (++s > nt) return true;
+          return false;
+        };
+        bool fin = false;
+        while (!fin && s < s_free) fin = chain(Parts<true, true, true, true>{});
+        while (!fin) fin = chain(Parts<true, true, true, false>{});
       }
-      if constexpr (PT::v) {
-        // dS of tile s - 1: P from role K times dP - D
-        f32x4_t P4[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) P4[a] = lds_read_f32x4(pfb + PV * PF + 1024u * a);
-        f32x16_t ds;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ds[i] = P4[i >> 2][i & 3] * dpacc[i];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) dsb[PV][ks] = pack_kstep(ds, ks);
+      step(Parts<false, false, false, false>{}, Stage<0>{}, nt + 1);   // role V's last step
+    } else {
+      // ------------------------------- role V -------------------------------
+      // (fewer live registers than role K: a deeper operand ring at d = 128)
+      constexpr int kRingV = D == 128 ? 8 : kRing;
+      bf16x8_t ringv[kRingV];
+      f32x16_t dpacc;        // dP - D of tile s (kept for the dS of the next step)
+      bf16x8_t dsb[2][2];    // [tile parity][k-step]: dS as C-part operands
+      constexpr int VPM = 3;   // vector instructions per C-part MFMA (1.5 per score)
+      auto step = [&](auto parts, auto stage, int s) {
+        using PT = decltype(parts);
+        constexpr int ST = decltype(stage)::value;
+        constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+        constexpr bool next = PT::v;   // the next step (if any) starts with a C part
+        using S = StepSeq<nc, na, PT::v ? VPM : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next,
+                          kRingV>;
+        constexpr uint32_t so_c = ((ST + NST - 2) % NST) * T::BYTES;   // tile s - 2
+        constexpr uint32_t so_n = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
+        constexpr uint32_t so_a = ST * T::BYTES;                       // tile s
+        constexpr int PC = ST & 1, PV = (ST + 1) & 1;   // parities of tiles s - 2 and s - 1
+        asm volatile("" : "+s"(s));
+        if (s + AHEAD < nt) request(s + AHEAD);
+        auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t {
+          return rQ.tr_opnd(so, i % ND, i / ND);
+        };
+        auto opnd = [&](int i) -> bf16x8_t {
+          if (i < nc) return c_opnd(so_c, i);
+          return rO.row_opnd(so_a, 0, i - nc);
+        };
+        if constexpr (!PT::c) {
+  #pragma unroll
+          for (int i = 0; i < kRingV && i < S::n; ++i) ringv[i] = opnd(i);
+        }
+        if constexpr (PT::v) {
+          // dS of tile s - 1: P from role K times dP - D
+          f32x4_t P4[4];
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) P4[a] = lds_read_f32x4(pfb + PV * PF + 1024u * a);
+          f32x16_t ds;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) ds[i] = P4[i >> 2][i & 3] * dpacc[i];
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) dsb[PV][ks] = pack_kstep(ds, ks);
+        }
+        // the dP accumulator starts from -D of the tile's rows
+        f32x16_t nd0;
+        if constexpr (PT::a) {
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4_t v4 =
+                lds_read_f32x4(ld + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
+          }
+        }
+  #pragma unroll
+        for (int i = 0; i < S::n; ++i) {
+          const bf16x8_t a = ringv[i % kRingV];
+          if (i + kRingV < S::n)
+            ringv[i % kRingV] = opnd(i + kRingV);
+          else if (next)
+            ringv[i % kRingV] = c_opnd(so_n, i + kRingV - S::n);
+          if (i < nc) {
+            acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
+          } else {
+            const int j = i - nc;
+            dpacc = mfma_32x32x16(a, kvf[j], j == 0 ? nd0 : dpacc);
+          }
+        }
+        sched_pattern<S>();
+        wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
+        __syncthreads();
+      };
+      step(Parts<false, false, false, false>{}, Stage<NST - 1>{}, -1);
+      step(Parts<false, false, true, false>{}, Stage<0>{}, 0);
+      step(Parts<false, true, true, false>{}, Stage<1>{}, 1);
+      {
+        using P = Parts<true, true, true, false>;
+        int s = 2;
+        for (;;) {
+          step(P{}, Stage<2>{}, s); if (++s > nt + 1) break;
+          step(P{}, Stage<3>{}, s); if (++s > nt + 1) break;
+          step(P{}, Stage<4>{}, s); if (++s > nt + 1) break;
+          step(P{}, Stage<5>{}, s); if (++s > nt + 1) break;
+          step(P{}, Stage<0>{}, s); if (++s > nt + 1) break;
+          step(P{}, Stage<1>{}, s); if (++s > nt + 1) break;
+        }
       }
-      // the dP accumulator starts from -D of the tile's rows
-      f32x16_t nd0;
-      if constexpr (PT::a) {
-#pragma unroll
+    }
+
+    // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
+    if (key < p.Tk) {
+      const Lay& lg = role_k ? p.ldv : p.ldk;
+      const size_t row = (size_t)(head_elem<D, GEN>(p, lg, bh, p.Tk) +
+                                  (int64_t)key * row_stride<D, GEN>(lg));
+      void* dst = role_k ? p.dv : p.dk;
+      const float sc = role_k ? 1.f : p.scale;
+  #pragma unroll
+      for (int db = 0; db < ND; ++db)
+  #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const f32x4_t v4 =
-              lds_read_f32x4(ld + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) nd0[4 * a + e] = v4[e];
+          const int col = 32 * db + 8 * a + 4 * g;
+          if (!GEN || col < hd)
+            store4<OUT_F32>(dst, row + col, sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
+                            sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
         }
-      }
-#pragma unroll
-      for (int i = 0; i < S::n; ++i) {
-        const bf16x8_t a = ringv[i % kRingV];
-        if (i + kRingV < S::n)
-          ringv[i % kRingV] = opnd(i + kRingV);
-        else if (next)
-          ringv[i % kRingV] = c_opnd(so_n, i + kRingV - S::n);
-        if (i < nc) {
-          acc[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], acc[i % ND]);
-        } else {
-          const int j = i - nc;
-          dpacc = mfma_32x32x16(a, kvf[j], j == 0 ? nd0 : dpacc);
-        }
-      }
-      sched_pattern<S>();
-      wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
-      __syncthreads();
-    };
-    step(Parts<false, false, false, false>{}, Stage<NST - 1>{}, -1);
-    step(Parts<false, false, true, false>{}, Stage<0>{}, 0);
-    step(Parts<false, true, true, false>{}, Stage<1>{}, 1);
-    {
-      using P = Parts<true, true, true, false>;
-      int s = 2;
-      for (;;) {
-        step(P{}, Stage<2>{}, s); if (++s > nt + 1) break;
-        step(P{}, Stage<3>{}, s); if (++s > nt + 1) break;
-        step(P{}, Stage<4>{}, s); if (++s > nt + 1) break;
-        step(P{}, Stage<5>{}, s); if (++s > nt + 1) break;
-        step(P{}, Stage<0>{}, s); if (++s > nt + 1) break;
-        step(P{}, Stage<1>{}, s); if (++s > nt + 1) break;
-      }
     }
-  }
-
-  // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
-  if (key < p.Tk) {
-    const Lay& lg = role_k ? p.ldv : p.ldk;
-    const size_t row = (size_t)(head_elem<D, GEN>(p, lg, bh, p.Tk) +
-                                (int64_t)key * row_stride<D, GEN>(lg));
-    void* dst = role_k ? p.dv : p.dk;
-    const float sc = role_k ? 1.f : p.scale;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = 32 * db + 8 * a + 4 * g;
-        if (!GEN || col < hd)
-          store4<OUT_F32>(dst, row + col, sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
-                          sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
-      }
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -921,11 +959,28 @@ hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   {
-    p.nblk = (a.Tk + kOwnK - 1) / kOwnK;
-    void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(
-        reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32, GEN>),
-        dim3(p.BH * p.nblk), dim3(kThreadsK), args, 0, stream);
+    // dK/dV: a persistent grid (each workgroup needs most of a CU's LDS and registers), one
+    // workgroup per CU in 8 XCD groups when there are more block pairs than CUs, else one per
+    // pair
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    BwdParams pk = p;
+    pk.nblk = (a.Tk + kOwnK - 1) / kOwnK;
+    const long long pairs = (long long)pk.BH * ((pk.nblk + 1) / 2);
+    int grid;
+    if (pairs > cus && cus >= 8) {
+      pk.groups = 8;
+      grid = cus - cus % 8;
+    } else {
+      pk.groups = 1;
+      grid = (int)(pairs < cus ? pairs : (cus > 0 ? cus : 1));
+    }
+    void* args[] = {&pk};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32, GEN>),
+                        dim3(grid), dim3(kThreadsK), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
