@@ -127,3 +127,36 @@ def test_bwd_causal_t1024_d64_full_size(gpu):
 
 def test_bwd_causal_t4096_d128_full_size(gpu):
     _full_size(gpu, "causal_b8_h32_t4096_d128", [(0, 0), (5, 9)])
+
+
+def test_bwd_persistent_schedule_more_pairs_than_cus(gpu):
+    """111 heads (not a multiple of the 8 XCD groups) and 9 key blocks per head (an odd count:
+    a middle block without a partner): 555 key-block pairs for the persistent dK/dV grid.  Every
+    gradient element is written (outputs start as NaN), and sampled heads, among them the last
+    heads of several groups, match the oracle."""
+    B, h, T, d = 3, 37, 1100, 128
+    log(f"[case] bwd persistent B={B} h={h} T={T} d={d}")
+    wl = si.custom_workload(B, h, T, T, d, True, name="bwd_persistent")
+    q, k, v = si.make_inputs(wl, 31)
+    do = si.make_grad(wl, 31)
+    qg, kg, vg, dog = to_gpu(q), to_gpu(k), to_gpu(v), to_gpu(do)
+    o_gpu, lse_gpu = gpu.fa_fwd(qg, kg, vg, causal=True, scale=wl.scale)
+    refs = {}
+    for bh in (0, 7, 8, 55, 103, 104, 109, 110):
+        b, hh = divmod(bh, h)
+        r, x64, o_bits, l32 = oracle_bwd_head(q[b, hh], k[b, hh], v[b, hh], do[b, hh], wl.scale,
+                                              True)
+        refs[(b, hh)] = (r, x64)
+        o_gpu[b, hh] = to_gpu(o_bits)
+        lse_gpu[b, hh] = torch.from_numpy(l32).cuda()
+    nan = float("nan")
+    dq = torch.full_like(qg, nan)
+    dk = torch.full_like(kg, nan)
+    dv = torch.full_like(vg, nan)
+    gpu.fa_bwd(qg, kg, vg, o_gpu, dog, lse_gpu, causal=True, scale=wl.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t.float()).all()), f"{name}: an element was not written"
+    res = {"dq16": dq, "dk16": dk, "dv16": dv}
+    for bh, (r, x64) in refs.items():
+        check_bwd_head("bwd persistent", res, bh, r, x64, wl.scale)
