@@ -234,10 +234,10 @@ __device__ __forceinline__ void block_of(const BwdParams& p, bool reverse, int& 
 // With groups == 8 workgroup n belongs to group n % 8 (the XCD it is dispatched to) and takes the
 // pairs of heads n % 8, n % 8 + 8, ..., so the tiles a head streams are shared in that XCD's L2.
 // body(bh, blk, tid) runs one item with tid, the thread index, rebuilt per item from the wave
-// index (a scalar) and the lane's position in the wave and passed through an opaque copy: every
-// lane-dependent value of an item is then computed inside it, so the compiler neither hoists such
-// values out of the item loop nor keeps them live across an item (the kernel's steady state
-// fills the registers).  The barrier between items lets the next item's loads reuse the LDS.
+// index (a scalar) and the lane's position in the wave, which an opaque instruction pair computes
+// inside the loop: every lane-dependent value of an item is then computed inside it, so the
+// compiler neither hoists such values out of the item loop nor keeps them live across an item
+// (the kernel's steady state fills the registers).  The barrier between items lets the next item's loads reuse the LDS.
 template <class F>
 __device__ __forceinline__ void for_each_block(const BwdParams& p, F&& body) {
   const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -253,8 +253,9 @@ __device__ __forceinline__ void for_each_block(const BwdParams& p, F&& body) {
     const int blk = (u & 1) ? j : p.nblk - 1 - j;
     if ((u & 1) && blk == p.nblk - 1 - j) continue;   // the middle block of an odd count
     if (u > 0) __syncthreads();
-    int tid = wave0 * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    asm volatile("" : "+v"(tid));
+    int ml;   // the lane's position, computed here (the builtins' result would be hoisted)
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ml));
+    const int tid = wave0 * 64 + ml;
     body(__builtin_amdgcn_readfirstlane(x + X * hl), __builtin_amdgcn_readfirstlane(blk), tid);
   }
 }
@@ -693,21 +694,58 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
 
     // ---- epilogue: register i of block db is column 32*db + 8*(i/4) + 4*g + i%4 of row `key`
-    if (key < p.Tk) {
-      const Lay& lg = role_k ? p.ldv : p.ldk;
-      const size_t row = (size_t)(head_elem<D, GEN>(p, lg, bh, p.Tk) +
-                                  (int64_t)key * row_stride<D, GEN>(lg));
-      void* dst = role_k ? p.dv : p.dk;
-      const float sc = role_k ? 1.f : p.scale;
+    const Lay& lg = role_k ? p.ldv : p.ldk;
+    const float sc = role_k ? 1.f : p.scale;
+    if constexpr (OUT_F32) {
+      if (key < p.Tk) {
+        const size_t row = (size_t)(head_elem<D, GEN>(p, lg, bh, p.Tk) +
+                                    (int64_t)key * row_stride<D, GEN>(lg));
+        void* dst = role_k ? p.dv : p.dk;
+  #pragma unroll
+        for (int db = 0; db < ND; ++db)
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int col = 32 * db + 8 * a + 4 * g;
+            if (!GEN || col < hd)
+              store4<OUT_F32>(dst, row + col, sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
+                              sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
+          }
+      }
+    } else {
+      // The wave's 32 rows pass through LDS (every stage is idle after the last step's barrier,
+      // and each wave uses only its own 32 rows) so that each store writes whole rows, 16 bytes
+      // per lane, instead of 16 bytes in each of 32 rows.  Row pitch 2D + 16 bytes: the 16-byte
+      // skew per row keeps both the 8-byte writes and the 16-byte reads free of bank conflicts.
+      constexpr uint32_t RS = 2 * D + 16;
+      constexpr int LPR = D / 8;      // lanes per row
+      constexpr int RPP = 64 / LPR;   // rows per store
+      static_assert(kWavesK * 32 * RS <= sizeof(lds), "epilogue rows exceed the stage area");
+      const uint32_t ew = lq + (uint32_t)wave * (32u * RS);
+      // the lane index rebuilt from values the steps keep live anyway (key, g)
+      const int ln = (key & 31) | (g << 5);
+      const uint32_t wr = ew + (uint32_t)(key & 31) * RS + 8u * (uint32_t)g;
   #pragma unroll
       for (int db = 0; db < ND; ++db)
   #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int col = 32 * db + 8 * a + 4 * g;
-          if (!GEN || col < hd)
-            store4<OUT_F32>(dst, row + col, sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
-                            sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]);
-        }
+        for (int a = 0; a < 4; ++a)
+          lds_write_u32x2(wr + 2u * (uint32_t)(32 * db + 8 * a),
+                          pack_bf16x4(sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
+                                      sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]));
+      const int rr = ln / LPR, cc = 8 * (ln % LPR);
+      const int key0 = key - (key & 31);
+      const uint32_t rs = row_stride<D, GEN>(lg);
+      // buffer stores: rows past the end and padded columns take an offset the range drops
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(
+          static_cast<uint16_t*>(role_k ? p.dv : p.dk) + head_elem<D, GEN>(p, lg, bh, p.Tk),
+          head_bytes(p.Tk, rs, hd));
+  #pragma unroll
+      for (int i = 0; i < 32 / RPP; ++i) {
+        const int r = RPP * i + rr;
+        const u32x4_t v = lds_read_u32x4(ew + (uint32_t)r * RS + 2u * (uint32_t)cc);
+        const bool ok = key0 + r < p.Tk && (!GEN || cc < hd);
+        const uint32_t off = ok ? 2u * ((uint32_t)(key0 + r) * rs + (uint32_t)cc) : kPadOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+      }
     }
   });
 }

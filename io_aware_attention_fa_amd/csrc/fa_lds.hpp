@@ -54,7 +54,16 @@ __device__ __forceinline__ f32x4_t lds_read_f32x4(uint32_t addr) {
   return *(lds_ptr_t)(uintptr_t)addr;
 }
 
-// 16-byte LDS writes at a byte address.
+__device__ __forceinline__ u32x4_t lds_read_u32x4(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const u32x4_t* lds_ptr_t;
+  return *(lds_ptr_t)(uintptr_t)addr;
+}
+
+// 8- and 16-byte LDS writes at a byte address.
+__device__ __forceinline__ void lds_write_u32x2(uint32_t addr, u32x2_t v) {
+  typedef __attribute__((address_space(3))) u32x2_t* lds_ptr_t;
+  *(lds_ptr_t)(uintptr_t)addr = v;
+}
 __device__ __forceinline__ void lds_write_f32x4(uint32_t addr, f32x4_t v) {
   typedef __attribute__((address_space(3))) f32x4_t* lds_ptr_t;
   *(lds_ptr_t)(uintptr_t)addr = v;
