@@ -207,6 +207,40 @@ __device__ __forceinline__ void store4(void* base, size_t elem, float a, float b
   }
 }
 
+// Stores a wave's 32 x D block of results as bf16: register i of acc[db] holds column
+// 32 db + 8 (i / 4) + 4 g + i % 4 of row row0 + l31 (l31 = lane % 32, g = lane / 32), scaled by
+// sc.  The rows pass through the wave's own 32 (2D + 16) bytes of LDS at ew (idle once the last
+// step's barrier has passed) so that each store writes whole rows, 16 bytes per lane, instead of
+// 16 bytes in each of 32 rows; the 16-byte skew per row keeps both the 8-byte writes and the
+// 16-byte reads free of bank conflicts.  Rows from nrows on and columns from hd on are dropped
+// by the buffer range (rd covers the head, rs is its row stride in elements).
+template <int D, bool GEN>
+__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[D / 32], float sc,
+                                                uint32_t ew, int l31, int g, int row0, int nrows,
+                                                __amdgpu_buffer_rsrc_t rd, uint32_t rs, int hd) {
+  constexpr uint32_t RS = 2 * D + 16;
+  constexpr int LPR = D / 8;      // lanes per row
+  constexpr int RPP = 64 / LPR;   // rows per store
+  const uint32_t wr = ew + (uint32_t)l31 * RS + 8u * (uint32_t)g;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      lds_write_u32x2(wr + 2u * (uint32_t)(32 * db + 8 * a),
+                      pack_bf16x4(sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
+                                  sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]));
+  const int ln = l31 | (g << 5);
+  const int rr = ln / LPR, cc = 8 * (ln % LPR);
+#pragma unroll
+  for (int i = 0; i < 32 / RPP; ++i) {
+    const int r = RPP * i + rr;
+    const u32x4_t v = lds_read_u32x4(ew + (uint32_t)r * RS + 2u * (uint32_t)cc);
+    const bool ok = row0 + r < nrows && (!GEN || cc < hd);
+    const uint32_t off = ok ? 2u * ((uint32_t)(row0 + r) * rs + (uint32_t)cc) : kPadOffset;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+  }
+}
+
 // Workgroup n -> (head, own block).  With groups == 8 the workgroups dispatched to one XCD
 // (n % 8) take the blocks of heads n % 8, n % 8 + 8, ... in order, so the tiles a head streams
 // are shared in that XCD's L2; `reverse` runs a head's blocks from the last one.
@@ -712,40 +746,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
           }
       }
     } else {
-      // The wave's 32 rows pass through LDS (every stage is idle after the last step's barrier,
-      // and each wave uses only its own 32 rows) so that each store writes whole rows, 16 bytes
-      // per lane, instead of 16 bytes in each of 32 rows.  Row pitch 2D + 16 bytes: the 16-byte
-      // skew per row keeps both the 8-byte writes and the 16-byte reads free of bank conflicts.
-      constexpr uint32_t RS = 2 * D + 16;
-      constexpr int LPR = D / 8;      // lanes per row
-      constexpr int RPP = 64 / LPR;   // rows per store
-      static_assert(kWavesK * 32 * RS <= sizeof(lds), "epilogue rows exceed the stage area");
-      const uint32_t ew = lq + (uint32_t)wave * (32u * RS);
-      // the lane index rebuilt from values the steps keep live anyway (key, g)
-      const int ln = (key & 31) | (g << 5);
-      const uint32_t wr = ew + (uint32_t)(key & 31) * RS + 8u * (uint32_t)g;
-  #pragma unroll
-      for (int db = 0; db < ND; ++db)
-  #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          lds_write_u32x2(wr + 2u * (uint32_t)(32 * db + 8 * a),
-                          pack_bf16x4(sc * acc[db][4 * a], sc * acc[db][4 * a + 1],
-                                      sc * acc[db][4 * a + 2], sc * acc[db][4 * a + 3]));
-      const int rr = ln / LPR, cc = 8 * (ln % LPR);
+      // the lane's row is key % 32 (key and g stay live through the steps; lane does not)
+      static_assert(kWavesK * 32 * (2 * D + 16) <= sizeof(lds), "rows exceed the stage area");
       const int key0 = key - (key & 31);
       const uint32_t rs = row_stride<D, GEN>(lg);
-      // buffer stores: rows past the end and padded columns take an offset the range drops
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(
           static_cast<uint16_t*>(role_k ? p.dv : p.dk) + head_elem<D, GEN>(p, lg, bh, p.Tk),
           head_bytes(p.Tk, rs, hd));
-  #pragma unroll
-      for (int i = 0; i < 32 / RPP; ++i) {
-        const int r = RPP * i + rr;
-        const u32x4_t v = lds_read_u32x4(ew + (uint32_t)r * RS + 2u * (uint32_t)cc);
-        const bool ok = key0 + r < p.Tk && (!GEN || cc < hd);
-        const uint32_t off = ok ? 2u * ((uint32_t)(key0 + r) * rs + (uint32_t)cc) : kPadOffset;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
-      }
+      store_rows_bf16<D, GEN>(acc, sc, lq + (uint32_t)wave * (32u * (2 * D + 16)), key & 31, g,
+                              key0, p.Tk, rd, rs, hd);
     }
   });
 }
@@ -939,19 +948,29 @@ void fa_bwd_dq_kernel(BwdParams p) {
     while (!fin) fin = chain(Parts<true, true, true, true>{});
   }
 
-  if (qrow < p.Tq) {
-    const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
-                                (int64_t)qrow * row_stride<D, GEN>(p.ldq));
+  if constexpr (OUT_F32 || GEN) {   // (through LDS the strided variant spills in its steps)
+    if (qrow < p.Tq) {
+      const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
+                                  (int64_t)qrow * row_stride<D, GEN>(p.ldq));
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = 32 * db + 8 * a + 4 * g;
-        if (!GEN || col < hd)
-          store4<OUT_F32>(p.dq, row + col, p.scale * accq[db][4 * a],
-                          p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
-                          p.scale * accq[db][4 * a + 3]);
-      }
+        for (int a = 0; a < 4; ++a) {
+          const int col = 32 * db + 8 * a + 4 * g;
+          if (!GEN || col < hd)
+            store4<OUT_F32>(p.dq, row + col, p.scale * accq[db][4 * a],
+                            p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
+                            p.scale * accq[db][4 * a + 3]);
+        }
+    }
+  } else {
+    static_assert(kWavesQ * 32 * (2 * D + 16) <= sizeof(lds), "dQ rows exceed the stage area");
+    const uint32_t rs = row_stride<D, GEN>(p.ldq);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(static_cast<uint16_t*>(p.dq) + head_elem<D, GEN>(p, p.ldq, bh, p.Tq),
+                  head_bytes(p.Tq, rs, hd));
+    store_rows_bf16<D, GEN>(accq, p.scale, lk + (uint32_t)wave * (32u * (2 * D + 16)),
+                            lane & 31, g, qw0, p.Tq, rd, rs, hd);
   }
 }
 
