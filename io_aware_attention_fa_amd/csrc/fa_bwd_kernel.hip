@@ -334,8 +334,9 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p, int64_t r
 //   A: the score-side products (S and dP) of the tile, from row operands in LDS;
 //   V: the elementwise part, P = exp2(S * scale * log2 e - L2), dS = P (dP - D), rounded to bf16;
 //   C: the gradient products that consume P and dS, from transposed operands in LDS.
-// A wave's step s runs C of an earlier tile with V of a later one scheduled between its MFMAs
-// (the vector instructions issue while the matrix core works), then A of the next tile; V reads
+// A wave's step s runs C of an earlier tile with V of a later one between its MFMAs (the vector
+// instructions issue while the matrix core works; the dQ kernel runs V first, having too few
+// registers for V's values and a deep operand ring at once), then A of the next tile; V reads
 // the score registers that A filled in the step before.  (dQ: C of tile s - 1, V of s, A of
 // s + 1; the two roles of the dK/dV kernel are listed there.)  The bf16 operands that V makes
 // for C are double-buffered by tile parity.  Every MFMA operand streams from LDS through a ring
@@ -348,46 +349,15 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p, int64_t r
 // run every part: their V and A parts read stages holding stale tiles and produce values that
 // are never used.
 
-// A step's MFMA stream: NC C-part MFMAs (two transposing reads each), then NA A-part MFMAs (one
-// read each), or the A part first if AFIRST.  PRE: the ring arrived preloaded; NEXT: the last
-// RING MFMAs read the next step's first operands (C operands, two reads each).  VPM vector
-// instructions are scheduled after each C-part MFMA (after each A-part MFMA when the step has
-// no C part), XR extra LDS reads are issued up front, and RING operands are in flight.
-template <int NC, int NA, int VPM, int XR, bool PRE, bool NEXT, int RING, bool AFIRST = false>
+// A step's MFMA stream: NC C-part MFMAs, then NA A-part MFMAs, with RING operands in flight.
+// The stream is issued in program order (a scheduling barrier after each MFMA): left to itself
+// the scheduler moved each operand read next to its MFMA, exposing the LDS latency once per
+// MFMA, and ran the V part's vector work apart from the MFMAs.
+template <int NC, int NA, int RING>
 struct StepSeq {
   static constexpr int n = NC + NA;
-  static constexpr int kRing = RING;
-  static_assert(n % kRing == 0, "the ring restarts at slot 0 every step");
-  static constexpr __device__ bool is_c(int i) { return AFIRST ? i >= NA : i < NC; }
-  static constexpr __device__ int reads(int i) { return is_c(i) ? 2 : 1; }
-  static constexpr __device__ int refill_reads(int i) {
-    return i + kRing < n ? reads(i + kRing) : (NEXT ? 2 : 0);
-  }
-  static constexpr __device__ int valu(int i) { return (NC > 0 ? is_c(i) : true) ? VPM : 0; }
-  static constexpr __device__ int initial_reads() {
-    int r = XR;
-    if (!PRE)
-      for (int i = 0; i < kRing && i < n; ++i) r += reads(i);
-    return r;
-  }
+  static_assert(n % RING == 0, "the ring restarts at slot 0 every step");
 };
-
-template <class S, int I>
-__device__ __forceinline__ void sched_step() {
-  if constexpr (I < S::n) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA I
-    if constexpr (S::refill_reads(I) > 0)
-      __builtin_amdgcn_sched_group_barrier(0x100, S::refill_reads(I), 0);   // its ring refill
-    if constexpr (S::valu(I) > 0) __builtin_amdgcn_sched_group_barrier(0x002, S::valu(I), 0);
-    sched_step<S, I + 1>();
-  }
-}
-template <class S>
-__device__ __forceinline__ void sched_pattern() {
-  if constexpr (S::initial_reads() > 0)
-    __builtin_amdgcn_sched_group_barrier(0x100, S::initial_reads(), 0);
-  sched_step<S, 0>();
-}
 
 // Packs registers 8*half .. +7 of a 16-register MFMA result block into one bf16 B operand
 // (RNE): the 16 streamed rows of one k-step.
@@ -558,9 +528,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         constexpr int ST = decltype(stage)::value;
         constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
         constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-        // vector instructions per C-part MFMA: about 4.5 per score with the mask, 2.5 without
-        constexpr int VPM = PT::m ? 9 : 5;
-        using S = StepSeq<nc, na, PT::v ? VPM : 0, PT::v ? 4 : 0, PT::c, next, kRing>;
+        using S = StepSeq<nc, na, kRing>;
         constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
         constexpr uint32_t so_v = ST * T::BYTES;                       // tile s
         constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;         // tile s + 1
@@ -578,27 +546,39 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   #pragma unroll
           for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
         }
+        // V part (P of tile s from its scores) in 8 chunks of two scores each
+        f32x4_t L4[4];
+        int lt = 0;
         if constexpr (PT::v) {
-          f32x4_t L4[4];
   #pragma unroll
           for (int a = 0; a < 4; ++a)
             L4[a] = lds_read_f32x4(ll + ST * (LDS_LD * 4) + 4u * (uint32_t)(8 * a + 4 * g));
-          const int lt = thr4 - (t0 + s) * R;
+          lt = thr4 - (t0 + s) * R;
+        }
+        auto vchunk = [&](int c) {
   #pragma unroll
-          for (int i = 0; i < 16; ++i) {
+          for (int i = 2 * c; i < 2 * c + 2; ++i) {
             const int a = i >> 2, e = i & 3;
             float pv = fast_exp2(__builtin_fmaf(sacc[i], p.c, -L4[a][e]));
             if (PT::m && 8 * a + e < lt) pv = 0.f;
             sacc[i] = pv;
           }
-  #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          if (c & 1) {
+            const int a = c >> 1;
             lds_write_f32x4(pfb + PV * PF + 1024u * a,
                             f32x4_t{sacc[4 * a], sacc[4 * a + 1], sacc[4 * a + 2],
                                     sacc[4 * a + 3]});
+          }
+          if (c == 3) pb[PV][0] = pack_kstep(sacc, 0);
+          if (c == 7) pb[PV][1] = pack_kstep(sacc, 1);
+        };
+        if constexpr (PT::v && !PT::c) {
   #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) pb[PV][ks] = pack_kstep(sacc, ks);
+          for (int c = 0; c < 8; ++c) vchunk(c);
         }
+        // MFMAs in program order (pinned by scheduling barriers): operand i + kRing is read
+        // while MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not
+        // depend on it (the A part overwrites the scores it reads, so it comes last).
   #pragma unroll
         for (int i = 0; i < S::n; ++i) {
           const bf16x8_t a = ring[i % kRing];
@@ -612,8 +592,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int j = i - nc;
             sacc = mfma_32x32x16(a, kvf[j], j == 0 ? f32x16_t{} : sacc);
           }
+          if constexpr (PT::v && PT::c) {
+            if (i < nc) {
+  #pragma unroll
+              for (int c = i * 8 / nc; c < (i + 1) * 8 / nc; ++c) vchunk(c);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        sched_pattern<S>();
         // the next step reads tile s + 2 (role K's S)
         wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
         __syncthreads();
@@ -645,14 +631,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       bf16x8_t ringv[kRingV];
       f32x16_t dpacc;        // dP - D of tile s (kept for the dS of the next step)
       bf16x8_t dsb[2][2];    // [tile parity][k-step]: dS as C-part operands
-      constexpr int VPM = 3;   // vector instructions per C-part MFMA (1.5 per score)
       auto step = [&](auto parts, auto stage, int s) {
         using PT = decltype(parts);
         constexpr int ST = decltype(stage)::value;
         constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
         constexpr bool next = PT::v;   // the next step (if any) starts with a C part
-        using S = StepSeq<nc, na, PT::v ? VPM : 0, (PT::v ? 4 : 0) + (PT::a ? 4 : 0), PT::c, next,
-                          kRingV>;
+        using S = StepSeq<nc, na, kRingV>;
         constexpr uint32_t so_c = ((ST + NST - 2) % NST) * T::BYTES;   // tile s - 2
         constexpr uint32_t so_n = ((ST + NST - 1) % NST) * T::BYTES;   // tile s - 1
         constexpr uint32_t so_a = ST * T::BYTES;                       // tile s
@@ -670,16 +654,22 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   #pragma unroll
           for (int i = 0; i < kRingV && i < S::n; ++i) ringv[i] = opnd(i);
         }
+        // V part: dS of tile s - 1 (P from role K times dP - D), in 8 chunks of two scores
+        f32x4_t P4[4];
+        f32x16_t ds;
         if constexpr (PT::v) {
-          // dS of tile s - 1: P from role K times dP - D
-          f32x4_t P4[4];
   #pragma unroll
           for (int a = 0; a < 4; ++a) P4[a] = lds_read_f32x4(pfb + PV * PF + 1024u * a);
-          f32x16_t ds;
+        }
+        auto vchunk = [&](int c) {
   #pragma unroll
-          for (int i = 0; i < 16; ++i) ds[i] = P4[i >> 2][i & 3] * dpacc[i];
+          for (int i = 2 * c; i < 2 * c + 2; ++i) ds[i] = P4[i >> 2][i & 3] * dpacc[i];
+          if (c == 3) dsb[PV][0] = pack_kstep(ds, 0);
+          if (c == 7) dsb[PV][1] = pack_kstep(ds, 1);
+        };
+        if constexpr (PT::v && !PT::c) {
   #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) dsb[PV][ks] = pack_kstep(ds, ks);
+          for (int c = 0; c < 8; ++c) vchunk(c);
         }
         // the dP accumulator starts from -D of the tile's rows
         f32x16_t nd0;
@@ -705,8 +695,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int j = i - nc;
             dpacc = mfma_32x32x16(a, kvf[j], j == 0 ? nd0 : dpacc);
           }
+          if constexpr (PT::v && PT::c) {
+            if (i < nc) {
+  #pragma unroll
+              for (int c = i * 8 / nc; c < (i + 1) * 8 / nc; ++c) vchunk(c);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        sched_pattern<S>();
         wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
         __syncthreads();
       };
@@ -772,16 +768,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int NK = R / 16;              // 16-key k-steps of the dQ product per tile
   constexpr int NST = 8;                  // LDS stages
   constexpr int AHEAD = 4;                // step s requests tile s + AHEAD
-  constexpr int kRing = 4;                // MFMA operands in flight
+  constexpr int kRing = 2;                // MFMA operands in flight (4 would spill)
   using T = BTile<D, R, kWavesQ>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int NA = 2 * KB * NS;   // S^T and dP^T MFMAs per tile
   constexpr int NC = ND * NK;       // dQ^T MFMAs per tile
-  // vector instructions per C-part MFMA: about 6.5 per score with the mask and 4.5 without,
-  // 16 * KB scores per lane
-  constexpr int VPM_M = (KB * 16 * 13 / 2 + NC - 1) / NC;
-  constexpr int VPM_U = (KB * 16 * 9 / 2 + NC - 1) / NC;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * NST * T::TILE];
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t lv = lk + NST * T::BYTES;
@@ -868,7 +860,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int ST = decltype(stage)::value;
     constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
     constexpr bool next = PT::v;
-    using S = StepSeq<nc, na, PT::v ? (PT::m ? VPM_M : VPM_U) : 0, 0, PT::c, next, kRing>;
+    using S = StepSeq<nc, na, kRing>;
     // s as an opaque scalar: otherwise the optimiser keeps a per-lane copy of each value derived
     // from it for every stage variant of the chain
     asm volatile("" : "+s"(s));
@@ -887,19 +879,29 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
     }
+    // V part (dS of tile s from its scores), in 8 chunks of 2 KB scores; k-step ks of dS is
+    // packed once the chunk holding its last score is done
+    const int lt = lim4 - s * R;   // lim relative to the tile's first key
+    auto vchunk = [&](int c) {
+      constexpr int PERC = 2 * KB;
+#pragma unroll
+      for (int f = c * PERC; f < (c + 1) * PERC; ++f) {
+        const int kb = f >> 4, i = f & 15;
+        float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
+        if (PT::m && 32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
+        dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        if ((8 * ks + 7) / PERC == c) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+    };
     if constexpr (PT::v) {
-      const int lt = lim4 - s * R;   // lim relative to the tile's first key
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
-          if (PT::m && 32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
-          dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
-        }
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+      for (int c = 0; c < 8; ++c) vchunk(c);
     }
+    // MFMAs in program order (pinned by scheduling barriers): operand i + kRing is read while
+    // MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not depend on it
+    // (the A part overwrites the scores it reads, so it comes last).
 #pragma unroll
     for (int i = 0; i < S::n; ++i) {
       const bf16x8_t a = ring[i % kRing];
@@ -916,8 +918,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
         else
           sacc[kb] = mfma_32x32x16(a, qf[ss], ss == 0 ? f32x16_t{} : sacc[kb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    sched_pattern<S>();
     wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
     __syncthreads();
   };
