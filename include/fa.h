@@ -184,8 +184,9 @@ int fa_decode_strided(const void* q, const void* k, const void* v, void* o, floa
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd / fa_bwd_f32 need: two fp32 values
- *   per query row (D_i and LSE_i * log2(e)), each array starting on a 256-byte boundary.
- *   Returns 0 for sizes < 1.
+ *   per query row (D_i and LSE_i * log2(e)), each array starting on a 256-byte boundary, then
+ *   1024 bytes of work counters for the dQ kernel's item queues (zeroed by the backward itself
+ *   on every call).  Returns 0 for sizes < 1.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq);
 
@@ -202,7 +203,8 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq);
  *   Tq x Tk is stored.  Masking as in fa_fwd (causal: query i sees key j iff j <= i + Tk - Tq).
  *   Precision: bf16 inputs, fp32 accumulation; P and dS are rounded to bf16 (round to nearest
  *   even) as operands of the gradient products; outputs rounded to bf16.  The result is
- *   deterministic (no atomics): the same inputs give the same bits.
+ *   deterministic (no atomic accumulation; which CU computes an item does not change its
+ *   bits): the same inputs give the same bits.
  *   d_head as fa_fwd (any multiple of 8 in [8, 128], padded to 64 or 128 with zeros on chip).
  *   Preconditions: as fa_fwd for sizes and alignment (all tensors 16-byte aligned, lse 4-byte);
  *   workspace 16-byte aligned with workspace_bytes >= fa_bwd_workspace_size(B, h, Tq); the

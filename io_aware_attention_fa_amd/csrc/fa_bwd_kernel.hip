@@ -10,15 +10,17 @@
 //
 // MI355X mapping (our design, not the pages'): three kernels on the caller's stream.
 //   * fa_bwd_prep: D_i and LSE_i * log2(e) per query row into the workspace (HBM-bound, one
-//     pass over O and dO).
-//   * fa_bwd_dkdv: one workgroup of 8 waves per (128-key block, head); each lane owns one key.
+//     pass over O and dO); it also zeroes the dQ kernel's item counters.
+//   * fa_bwd_dkdv: persistent workgroups of 8 waves, each running (128-key block, head) items
+//     dealt as pairs of blocks with equal total work; each lane owns one key.
 //     Q, dO and the per-row L, D stream through LDS in 32-row tiles; K and V stay in registers
 //     as MFMA B operands.  The two waves on a SIMD own the same 32 keys and split the work: one
 //     computes S = Q K^T, P and dV^T += dO^T P, the other dP = dO V^T, dS and dK^T += Q^T dS;
 //     P goes from the first to the second through LDS.  dO^T and Q^T come from the transposing
 //     LDS read (ds_read_b64_tr_b16) of the same row-major tiles.  No atomics: every key's dK
 //     and dV are finished by one workgroup.
-//   * fa_bwd_dq: one workgroup of 8 waves per (256-query block, head); each lane owns one query.
+//   * fa_bwd_dq: persistent workgroups of 8 waves, each taking (256-query block, head) items
+//     from XCD-local queues (an atomic counter each) until none is left; each lane owns one query.
 //     K and V stream through LDS; S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
 //     dQ^T += K^T dS^T with K^T from the transposing read.  The two gradient kernels share no
 //     partial sums, so the result is deterministic.
@@ -53,6 +55,9 @@ constexpr int kThreadsK = 64 * kWavesK;
 constexpr int kWavesQ = 8;    // dQ: two waves per SIMD, 32 own queries each
 constexpr int kOwnQ = 32 * kWavesQ;
 constexpr int kThreadsQ = 64 * kWavesQ;
+constexpr int kQueues = 8;     // XCD groups of the persistent kernels; dQ's item queues
+// the workspace reserves 1 KB for dQ's item counters, 64 bytes apart
+static_assert(kQueues * 64 <= 1024, "counters exceed their workspace area");
 
 // Layout of one [B][h][T][d] tensor: element (b, h, t, c) at base[b*sb + h*sh + t*st + c].
 struct Lay {
@@ -72,8 +77,9 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
+  uint32_t* ctr;          // dQ's item counters (workspace, 64 B apart; the preprocess zeroes)
   int Tq, Tk, BH, nblk;   // nblk: own blocks (128 keys or 256 queries) per head
-  int groups;             // 8: workgroup n works on heads n % 8, n % 8 + 8, ... (XCD-local)
+  int groups;             // XCD groups: group x works on heads x, x + groups, ...
   float c;                // scale * log2(e)
   float scale;
   // general layouts (used by the GEN variants): heads per batch entry, the true head dim
@@ -241,25 +247,6 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[D / 32], f
   }
 }
 
-// Workgroup n -> (head, own block).  With groups == 8 the workgroups dispatched to one XCD
-// (n % 8) take the blocks of heads n % 8, n % 8 + 8, ... in order, so the tiles a head streams
-// are shared in that XCD's L2; `reverse` runs a head's blocks from the last one.
-__device__ __forceinline__ void block_of(const BwdParams& p, bool reverse, int& bh, int& blk) {
-  const int n = blockIdx.x;
-  int hl, j;
-  if (p.groups == 8) {
-    const int x = n & 7, c = n >> 3;
-    hl = c / p.nblk;
-    j = c - hl * p.nblk;
-    hl = x + 8 * hl;
-  } else {
-    hl = n / p.nblk;
-    j = n - hl * p.nblk;
-  }
-  bh = __builtin_amdgcn_readfirstlane(hl);
-  blk = __builtin_amdgcn_readfirstlane(reverse ? p.nblk - 1 - j : j);
-}
-
 // Persistent schedule of the dK/dV kernel: at most one workgroup per CU, each running several
 // (head, key block) items one after the other, so that a CU starts its next block without a new
 // workgroup's dispatch (which cost about as much as 15-20 of its pipeline steps).  Blocks are
@@ -291,6 +278,84 @@ __device__ __forceinline__ void for_each_block(const BwdParams& p, F&& body) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ml));
     const int tid = wave0 * 64 + ml;
     body(__builtin_amdgcn_readfirstlane(x + X * hl), __builtin_amdgcn_readfirstlane(blk), tid);
+  }
+}
+
+// Persistent schedule of the dQ kernel: at most one workgroup per CU, each taking (head, query
+// block) items from shared queues until none is left, so that no CU idles while items remain
+// (a fixed deal ends with the slowest XCD; the XCDs of one device differ in speed by several
+// percent).  Queue x < groups holds the items of heads x, x + groups, ... head by head, nblk per
+// head, and counter x (ctr[16 x], 64 bytes apart; the preprocess zeroes them) counts the items
+// taken.  Workgroup n takes from queue n % groups (with groups == 8, the queue of the XCD it is
+// dispatched to: the workgroups working on a head at one time share its streamed tiles in their
+// L2) and, once that queue is empty, from the others in turn.  With REV a head's blocks are
+// taken from the last one, which under the causal mask sees the most keys, so the items left at
+// the end are the short ones.  (The dK/dV kernel keeps the fixed deal of pairs above: taken from
+// queues its items ran 2-3% slower.)
+
+// Items of queue x.
+__device__ __forceinline__ int queue_items(const BwdParams& p, int x) {
+  return ((p.BH - x + p.groups - 1) / p.groups) * p.nblk;
+}
+
+// Completes taking an item (one lane): k0 is what the counter of queue x0 returned.  If that
+// queue is empty, takes from the others in turn.  x = the item's queue (-1: none left), k = its
+// index there.
+__device__ __forceinline__ void take_item(const BwdParams& p, uint32_t* ctr, int x0, int k0,
+                                          int& x, int& k) {
+  x = x0;
+  k = k0;
+  if (k < queue_items(p, x)) return;
+  for (int q = 1; q < p.groups; ++q) {
+    x = x0 + q;
+    if (x >= p.groups) x -= p.groups;
+    k = (int)atomicAdd(ctr + 16 * x, 1u);
+    if (k < queue_items(p, x)) return;
+  }
+  x = -1;
+}
+
+// Runs body(bh, blk, tid, claim, publish) for every item this workgroup takes.  One lane (lane 0
+// of wave 0) takes items; the item is passed to the waves through a two-int LDS slot.  The body
+// calls claim() as its first loads are issued (the counter's atomic then completes with them:
+// its result is read only after the body has waited for all of its loads) and publish(c) after
+// its first barrier (every wave has read the slot by then).  tid is the thread index, rebuilt
+// per item as in for_each_block.  The barrier between items lets the next item's loads reuse
+// the LDS.
+template <bool REV, class F>
+__device__ __forceinline__ void for_each_item(const BwdParams& p, uint32_t* ctr, int* slot,
+                                              F&& body) {
+  const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int x0 = (int)blockIdx.x % p.groups;
+  auto lane_pos = []() {
+    int ml;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ml));
+    return ml;
+  };
+  auto claim = [&]() -> int {
+    int k0 = 0;
+    if (wave0 == 0 && lane_pos() == 0) k0 = (int)atomicAdd(ctr + 16 * x0, 1u);
+    return k0;
+  };
+  auto publish = [&](int k0) {
+    if (wave0 == 0 && lane_pos() == 0) {
+      int x, k;
+      take_item(p, ctr, x0, k0, x, k);
+      slot[0] = x;
+      slot[1] = k;
+    }
+  };
+  publish(claim());
+  __syncthreads();
+  for (;;) {
+    const int x = __builtin_amdgcn_readfirstlane(slot[0]);
+    if (x < 0) break;
+    const int k = __builtin_amdgcn_readfirstlane(slot[1]);
+    const int hl = k / p.nblk, r = k - hl * p.nblk;
+    body(__builtin_amdgcn_readfirstlane(x + p.groups * hl),
+         __builtin_amdgcn_readfirstlane(REV ? p.nblk - 1 - r : r), wave0 * 64 + lane_pos(), claim,
+         publish);
+    __syncthreads();
   }
 }
 
@@ -327,6 +392,7 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p, int64_t r
     p.dd[row] = -acc;
     p.l2[row] = p.lse[row] * kLog2e;
   }
+  if (blockIdx.x == 0 && threadIdx.x < kQueues) p.ctr[16 * threadIdx.x] = 0u;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -390,7 +456,7 @@ __device__ __forceinline__ void wait_tile(int need, int last) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup of 8 waves per (128-key block, head), lane = key; query tiles of 32 rows.
+// dK, dV: 8 waves per (128-key block, head) item, lane = key; query tiles of 32 rows.
 // Waves w and w + 4 (which share a SIMD) own the same 32 keys and split the work: wave w (role K)
 // holds the K rows and computes S, P and dV; wave w + 4 (role V) holds the V rows and computes
 // dP - D, dS and dK.  P goes from role K to role V through LDS (fp32, double-buffered by tile
@@ -756,8 +822,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup of 8 waves (two per SIMD) per (256-query block, head); lane = query; key
-// tiles of 32 rows (d = 128) or 64 rows (d = 64).  The per-wave state fits in half of a SIMD's
+// dQ: 8 waves (two per SIMD) per (256-query block, head) item; lane = query; key tiles of 32
+// rows (d = 128) or 64 rows (d = 64).  The per-wave state fits in half of a SIMD's
 // registers, so the two waves of a SIMD overlap one's LDS reads and vector work with the
 // other's MFMAs.
 template <int D, bool CAUSAL, bool OUT_F32, bool GEN>
@@ -778,202 +844,207 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const uint32_t lk = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   const uint32_t lv = lk + NST * T::BYTES;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;
-  const Lanes<D, R, kWavesQ> ln(wave, lane);
+  __shared__ int slot[2];
+  // causal: a head's last query blocks (the longest key ranges) first
+  for_each_item<CAUSAL>(p, p.ctr, slot, [&](const int bh, const int blk, const int tid,
+                                            auto&& claim, auto&& publish) {
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const Lanes<D, R, kWavesQ> ln(wave, lane);
 
-  int bh, blk;
-  block_of(p, CAUSAL, bh, blk);   // causal: the longest key ranges (last query blocks) first
-  const int off = p.Tk - p.Tq;
-  const int i0 = blk * kOwnQ;
-  const int qw0 = i0 + wave * 32;
-  const int qrow = qw0 + (lane & 31);
-  // keys above lim get P = 0 (past the end, or above the diagonal); lim4 is lim relative to the
-  // first key this lane holds in a tile
-  const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
-  const int lim4 = lim - 4 * g;
-  // Tiles before s_mask need no mask (wave-uniform): their last key is within the limit of
-  // this wave's first query.
-  const int lim_w = CAUSAL ? min(p.Tk - 1, qw0 + off) : p.Tk - 1;
-  const int s_mask = (lim_w + 1) / R;
+    const int off = p.Tk - p.Tq;
+    const int i0 = blk * kOwnQ;
+    const int qw0 = i0 + wave * 32;
+    const int qrow = qw0 + (lane & 31);
+    // keys above lim get P = 0 (past the end, or above the diagonal); lim4 is lim relative to the
+    // first key this lane holds in a tile
+    const int lim = CAUSAL ? min(p.Tk - 1, qrow + off) : p.Tk - 1;
+    const int lim4 = lim - 4 * g;
+    // Tiles before s_mask need no mask (wave-uniform): their last key is within the limit of
+    // this wave's first query.
+    const int lim_w = CAUSAL ? min(p.Tk - 1, qw0 + off) : p.Tk - 1;
+    const int s_mask = (lim_w + 1) / R;
 
-  // Q and dO rows of this lane's query as B operands, and its L2 and -D.
-  const int hd = GEN ? p.d : D;   // true head dim
-  bf16x8_t qf[NS], dof[NS];
-  float l2q = 0.f, ndq = 0.f;
-  {
-    const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
-                                                head_bytes(p.Tq, st_q, hd));
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
-                                                 head_bytes(p.Tq, st_do, hd));
+    // Q and dO rows of this lane's query as B operands, and its L2 and -D.
+    const int hd = GEN ? p.d : D;   // true head dim
+    bf16x8_t qf[NS], dof[NS];
+    float l2q = 0.f, ndq = 0.f;
+    {
+      const uint32_t st_q = row_stride<D, GEN>(p.lq), st_do = row_stride<D, GEN>(p.ldo);
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_elem<D, GEN>(p, p.lq, bh, p.Tq),
+                                                  head_bytes(p.Tq, st_q, hd));
+      const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head_elem<D, GEN>(p, p.ldo, bh, p.Tq),
+                                                   head_bytes(p.Tq, st_do, hd));
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qf[s] = as_bf16x8(buf_load16(rq, off16(qrow, 16 * s + 8 * g, st_q, hd)));
-      dof[s] = as_bf16x8(buf_load16(rdo, off16(qrow, 16 * s + 8 * g, st_do, hd)));
+      for (int s = 0; s < NS; ++s) {
+        qf[s] = as_bf16x8(buf_load16(rq, off16(qrow, 16 * s + 8 * g, st_q, hd)));
+        dof[s] = as_bf16x8(buf_load16(rdo, off16(qrow, 16 * s + 8 * g, st_do, hd)));
+      }
+      if (qrow < p.Tq) {
+        l2q = p.l2[(size_t)bh * p.Tq + qrow];
+        ndq = p.dd[(size_t)bh * p.Tq + qrow];
+      }
     }
-    if (qrow < p.Tq) {
-      l2q = p.l2[(size_t)bh * p.Tq + qrow];
-      ndq = p.dd[(size_t)bh * p.Tq + qrow];
-    }
-  }
 
-  int kend = p.Tk;
-  if (CAUSAL) kend = min(p.Tk, min(i0 + kOwnQ, p.Tq) + off);
-  const int nt = __builtin_amdgcn_readfirstlane((kend + R - 1) / R);
+    int kend = p.Tk;
+    if (CAUSAL) kend = min(p.Tk, min(i0 + kOwnQ, p.Tq) + off);
+    const int nt = __builtin_amdgcn_readfirstlane((kend + R - 1) / R);
 
-  const uint32_t st_k = row_stride<D, GEN>(p.lk), st_v = row_stride<D, GEN>(p.lv);
-  const u32x4_t rk = rsrc_words(p.k + head_elem<D, GEN>(p, p.lk, bh, p.Tk),
-                                head_bytes(p.Tk, st_k, hd));
-  const u32x4_t rv = rsrc_words(p.v + head_elem<D, GEN>(p, p.lv, bh, p.Tk),
-                                head_bytes(p.Tk, st_v, hd));
-  uint32_t gk[T::LPW], gv[T::LPW];   // this wave's global load offsets within a tile
-#pragma unroll
-  for (int i = 0; i < T::LPW; ++i) {
-    gk[i] = ln.goff(i, st_k, hd);
-    gv[i] = ln.goff(i, st_v, hd);
-  }
-  auto request = [&](int it) {
-    const int st = it & (NST - 1);
-    const uint32_t g0k = (uint32_t)it * (R * 2u) * st_k, g0v = (uint32_t)it * (R * 2u) * st_v;
+    const uint32_t st_k = row_stride<D, GEN>(p.lk), st_v = row_stride<D, GEN>(p.lv);
+    const u32x4_t rk = rsrc_words(p.k + head_elem<D, GEN>(p, p.lk, bh, p.Tk),
+                                  head_bytes(p.Tk, st_k, hd));
+    const u32x4_t rv = rsrc_words(p.v + head_elem<D, GEN>(p, p.lv, bh, p.Tk),
+                                  head_bytes(p.Tk, st_v, hd));
+    uint32_t gk[T::LPW], gv[T::LPW];   // this wave's global load offsets within a tile
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i) {
-      lds_dma16(rk, lk + st * T::BYTES + ln.dma_l[i], g0k + gk[i]);
-      lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0v + gv[i]);
+      gk[i] = ln.goff(i, st_k, hd);
+      gv[i] = ln.goff(i, st_v, hd);
     }
-  };
-  constexpr int PER = 2 * T::LPW;
-
-  f32x16_t accq[ND];
+    auto request = [&](int it) {
+      const int st = it & (NST - 1);
+      const uint32_t g0k = (uint32_t)it * (R * 2u) * st_k, g0v = (uint32_t)it * (R * 2u) * st_v;
 #pragma unroll
-  for (int db = 0; db < ND; ++db) accq[db] = f32x16_t{};
-  f32x16_t sacc[KB], dpacc[KB];   // [32-key block]: S^T, dP^T (then dS^T)
-  bf16x8_t dsb[2][NK];            // [tile parity][k-step]: dS^T as C operands
-  bf16x8_t ring[kRing];
-  const Region<D> rK(lk, ln.row_off, ln.tr_off), rV(lv, ln.row_off, ln.tr_off);
-
-  // Step s with stage ST = s % NST.  Register i of 32-key block kb holds key
-  // R*s + 32*kb + 8*(i/4) + 4*g + i%4 for query `qrow`.
-  auto step = [&](auto parts, auto stage, int s) {
-    using PT = decltype(parts);
-    constexpr int ST = decltype(stage)::value;
-    constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
-    constexpr bool next = PT::v;
-    using S = StepSeq<nc, na, kRing>;
-    // s as an opaque scalar: otherwise the optimiser keeps a per-lane copy of each value derived
-    // from it for every stage variant of the chain
-    asm volatile("" : "+s"(s));
-    constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;
-    constexpr uint32_t so_v = ST * T::BYTES;
-    constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;
-    constexpr int PC = (ST + 1) & 1, PV = ST & 1;
-    if (s + AHEAD < nt) request(s + AHEAD);
-    auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rK.tr_opnd(so, i % ND, i / ND); };
-    auto opnd = [&](int i) -> bf16x8_t {
-      if (i < nc) return c_opnd(so_c, i);
-      const int j = i - nc;
-      return ((j & 1) ? rV : rK).row_opnd(so_a, (j >> 1) % KB, (j >> 1) / KB);
-    };
-    if constexpr (!PT::c) {
-#pragma unroll
-      for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
-    }
-    // V part (dS of tile s from its scores), in 8 chunks of 2 KB scores; k-step ks of dS is
-    // packed once the chunk holding its last score is done
-    const int lt = lim4 - s * R;   // lim relative to the tile's first key
-    auto vchunk = [&](int c) {
-      constexpr int PERC = 2 * KB;
-#pragma unroll
-      for (int f = c * PERC; f < (c + 1) * PERC; ++f) {
-        const int kb = f >> 4, i = f & 15;
-        float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
-        if (PT::m && 32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
-        dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
+      for (int i = 0; i < T::LPW; ++i) {
+        lds_dma16(rk, lk + st * T::BYTES + ln.dma_l[i], g0k + gk[i]);
+        lds_dma16(rv, lv + st * T::BYTES + ln.dma_l[i], g0v + gv[i]);
       }
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks)
-        if ((8 * ks + 7) / PERC == c) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
     };
-    if constexpr (PT::v) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) vchunk(c);
-    }
-    // MFMAs in program order (pinned by scheduling barriers): operand i + kRing is read while
-    // MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not depend on it
-    // (the A part overwrites the scores it reads, so it comes last).
-#pragma unroll
-    for (int i = 0; i < S::n; ++i) {
-      const bf16x8_t a = ring[i % kRing];
-      if (i + kRing < S::n)
-        ring[i % kRing] = opnd(i + kRing);
-      else if (next)
-        ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
-      if (i < nc) {
-        accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
-      } else {
-        const int j = i - nc, ss = (j >> 1) / KB, kb = (j >> 1) % KB;
-        if (j & 1)
-          dpacc[kb] = mfma_32x32x16(a, dof[ss], ss == 0 ? f32x16_t{} : dpacc[kb]);
-        else
-          sacc[kb] = mfma_32x32x16(a, qf[ss], ss == 0 ? f32x16_t{} : sacc[kb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
-    __syncthreads();
-  };
-  for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
-  wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));
-  __syncthreads();
-  step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
-  step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
-  // steps 1 .. nt: a chain of the NST stage variants, left after step nt; each step in a masked
-  // or an unmasked variant (the mask costs two vector instructions per score)
-  {
-    // whole chains of the NST stage variants without the mask while every step of a chain is
-    // before s_mask, then chains with it (each chain left after step nt)
-    int s = 1;
-    auto chain = [&](auto parts) {
-      step(parts, Stage<1>{}, s); if (++s > nt) return true;
-      step(parts, Stage<2>{}, s); if (++s > nt) return true;
-      step(parts, Stage<3>{}, s); if (++s > nt) return true;
-      step(parts, Stage<4>{}, s); if (++s > nt) return true;
-      step(parts, Stage<5>{}, s); if (++s > nt) return true;
-      step(parts, Stage<6>{}, s); if (++s > nt) return true;
-      step(parts, Stage<7>{}, s); if (++s > nt) return true;
-      step(parts, Stage<0>{}, s); if (++s > nt) return true;
-      return false;
-    };
-    bool fin = false;
-    while (!fin && s + NST <= s_mask) fin = chain(Parts<true, true, true, false>{});
-    while (!fin) fin = chain(Parts<true, true, true, true>{});
-  }
+    constexpr int PER = 2 * T::LPW;
 
-  if constexpr (OUT_F32 || GEN) {   // (through LDS the strided variant spills in its steps)
-    if (qrow < p.Tq) {
-      const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
-                                  (int64_t)qrow * row_stride<D, GEN>(p.ldq));
+    f32x16_t accq[ND];
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+    for (int db = 0; db < ND; ++db) accq[db] = f32x16_t{};
+    f32x16_t sacc[KB], dpacc[KB];   // [32-key block]: S^T, dP^T (then dS^T)
+    bf16x8_t dsb[2][NK];            // [tile parity][k-step]: dS^T as C operands
+    bf16x8_t ring[kRing];
+    const Region<D> rK(lk, ln.row_off, ln.tr_off), rV(lv, ln.row_off, ln.tr_off);
+
+    // Step s with stage ST = s % NST.  Register i of 32-key block kb holds key
+    // R*s + 32*kb + 8*(i/4) + 4*g + i%4 for query `qrow`.
+    auto step = [&](auto parts, auto stage, int s) {
+      using PT = decltype(parts);
+      constexpr int ST = decltype(stage)::value;
+      constexpr int nc = PT::c ? NC : 0, na = PT::a ? NA : 0;
+      constexpr bool next = PT::v;
+      using S = StepSeq<nc, na, kRing>;
+      // s as an opaque scalar: otherwise the optimiser keeps a per-lane copy of each value derived
+      // from it for every stage variant of the chain
+      asm volatile("" : "+s"(s));
+      constexpr uint32_t so_c = ((ST + NST - 1) % NST) * T::BYTES;
+      constexpr uint32_t so_v = ST * T::BYTES;
+      constexpr uint32_t so_a = ((ST + 1) % NST) * T::BYTES;
+      constexpr int PC = (ST + 1) & 1, PV = ST & 1;
+      if (s + AHEAD < nt) request(s + AHEAD);
+      auto c_opnd = [&](uint32_t so, int i) -> bf16x8_t { return rK.tr_opnd(so, i % ND, i / ND); };
+      auto opnd = [&](int i) -> bf16x8_t {
+        if (i < nc) return c_opnd(so_c, i);
+        const int j = i - nc;
+        return ((j & 1) ? rV : rK).row_opnd(so_a, (j >> 1) % KB, (j >> 1) / KB);
+      };
+      if constexpr (!PT::c) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int col = 32 * db + 8 * a + 4 * g;
-          if (!GEN || col < hd)
-            store4<OUT_F32>(p.dq, row + col, p.scale * accq[db][4 * a],
-                            p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
-                            p.scale * accq[db][4 * a + 3]);
+        for (int i = 0; i < kRing && i < S::n; ++i) ring[i] = opnd(i);
+      }
+      // V part (dS of tile s from its scores), in 8 chunks of 2 KB scores; k-step ks of dS is
+      // packed once the chunk holding its last score is done
+      const int lt = lim4 - s * R;   // lim relative to the tile's first key
+      auto vchunk = [&](int c) {
+        constexpr int PERC = 2 * KB;
+#pragma unroll
+        for (int f = c * PERC; f < (c + 1) * PERC; ++f) {
+          const int kb = f >> 4, i = f & 15;
+          float pv = fast_exp2(__builtin_fmaf(sacc[kb][i], p.c, -l2q));
+          if (PT::m && 32 * kb + 8 * (i >> 2) + (i & 3) > lt) pv = 0.f;
+          dpacc[kb][i] = pv * (dpacc[kb][i] + ndq);
         }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
+          if ((8 * ks + 7) / PERC == c) dsb[PV][ks] = pack_kstep(dpacc[ks >> 1], ks & 1);
+      };
+      if constexpr (PT::v) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) vchunk(c);
+      }
+      // MFMAs in program order (pinned by scheduling barriers): operand i + kRing is read while
+      // MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not depend on it
+      // (the A part overwrites the scores it reads, so it comes last).
+#pragma unroll
+      for (int i = 0; i < S::n; ++i) {
+        const bf16x8_t a = ring[i % kRing];
+        if (i + kRing < S::n)
+          ring[i % kRing] = opnd(i + kRing);
+        else if (next)
+          ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
+        if (i < nc) {
+          accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
+        } else {
+          const int j = i - nc, ss = (j >> 1) / KB, kb = (j >> 1) % KB;
+          if (j & 1)
+            dpacc[kb] = mfma_32x32x16(a, dof[ss], ss == 0 ? f32x16_t{} : dpacc[kb]);
+          else
+            sacc[kb] = mfma_32x32x16(a, qf[ss], ss == 0 ? f32x16_t{} : sacc[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
+      __syncthreads();
+    };
+    for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
+    const int next = claim();
+    wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));
+    __syncthreads();
+    publish(next);
+    step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
+    step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
+    // steps 1 .. nt: a chain of the NST stage variants, left after step nt; each step in a masked
+    // or an unmasked variant (the mask costs two vector instructions per score)
+    {
+      // whole chains of the NST stage variants without the mask while every step of a chain is
+      // before s_mask, then chains with it (each chain left after step nt)
+      int s = 1;
+      auto chain = [&](auto parts) {
+        step(parts, Stage<1>{}, s); if (++s > nt) return true;
+        step(parts, Stage<2>{}, s); if (++s > nt) return true;
+        step(parts, Stage<3>{}, s); if (++s > nt) return true;
+        step(parts, Stage<4>{}, s); if (++s > nt) return true;
+        step(parts, Stage<5>{}, s); if (++s > nt) return true;
+        step(parts, Stage<6>{}, s); if (++s > nt) return true;
+        step(parts, Stage<7>{}, s); if (++s > nt) return true;
+        step(parts, Stage<0>{}, s); if (++s > nt) return true;
+        return false;
+      };
+      bool fin = false;
+      while (!fin && s + NST <= s_mask) fin = chain(Parts<true, true, true, false>{});
+      while (!fin) fin = chain(Parts<true, true, true, true>{});
     }
-  } else {
-    static_assert(kWavesQ * 32 * (2 * D + 16) <= sizeof(lds), "dQ rows exceed the stage area");
-    const uint32_t rs = row_stride<D, GEN>(p.ldq);
-    const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(static_cast<uint16_t*>(p.dq) + head_elem<D, GEN>(p, p.ldq, bh, p.Tq),
-                  head_bytes(p.Tq, rs, hd));
-    store_rows_bf16<D, GEN>(accq, p.scale, lk + (uint32_t)wave * (32u * (2 * D + 16)),
-                            lane & 31, g, qw0, p.Tq, rd, rs, hd);
-  }
+
+    if constexpr (OUT_F32 || GEN) {   // (through LDS the strided variant spills in its steps)
+      if (qrow < p.Tq) {
+        const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
+                                    (int64_t)qrow * row_stride<D, GEN>(p.ldq));
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int col = 32 * db + 8 * a + 4 * g;
+            if (!GEN || col < hd)
+              store4<OUT_F32>(p.dq, row + col, p.scale * accq[db][4 * a],
+                              p.scale * accq[db][4 * a + 1], p.scale * accq[db][4 * a + 2],
+                              p.scale * accq[db][4 * a + 3]);
+          }
+      }
+    } else {
+      static_assert(kWavesQ * 32 * (2 * D + 16) <= sizeof(lds), "dQ rows exceed the stage area");
+      const uint32_t rs = row_stride<D, GEN>(p.ldq);
+      const __amdgpu_buffer_rsrc_t rd =
+          make_rsrc(static_cast<uint16_t*>(p.dq) + head_elem<D, GEN>(p, p.ldq, bh, p.Tq),
+                    head_bytes(p.Tq, rs, hd));
+      store_rows_bf16<D, GEN>(accq, p.scale, lk + (uint32_t)wave * (32u * (2 * D + 16)),
+                              lane & 31, g, qw0, p.Tq, rd, rs, hd);
+    }
+  });
 }
 
 Lay to_lay(const int64_t* s3) { return Lay{s3[0], s3[1], (uint32_t)s3[2]}; }
@@ -997,7 +1068,8 @@ hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
   p.BH = a.B * a.H;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  p.groups = (p.BH % 8 == 0) ? 8 : 1;
+  p.ctr = a.ctr;
+  p.groups = 1;
   p.H = a.H;
   p.d = a.d;
   p.lq = to_lay(a.q_s);
@@ -1018,36 +1090,36 @@ hipError_t launch(const BwdLaunch& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   {
-    // dK/dV: a persistent grid (each workgroup needs most of a CU's LDS and registers), one
-    // workgroup per CU in 8 XCD groups when there are more block pairs than CUs, else one per
-    // pair
+    // both gradient kernels are persistent: one workgroup per CU (each needs most of a CU's LDS
+    // and registers), at most one per work unit; 8 XCD groups when there are more units than CUs
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    if (cus < 1) cus = 1;
+    auto grid_for = [&](BwdParams& q, long long units) {
+      if (units > cus && cus >= kQueues) {
+        q.groups = kQueues;
+        return cus - cus % kQueues;
+      }
+      q.groups = 1;
+      return (int)(units < cus ? units : cus);
+    };
+    // dK/dV: (nblk - 1 - j, j) key-block pairs dealt to the workgroups
     BwdParams pk = p;
     pk.nblk = (a.Tk + kOwnK - 1) / kOwnK;
-    const long long pairs = (long long)pk.BH * ((pk.nblk + 1) / 2);
-    int grid;
-    if (pairs > cus && cus >= 8) {
-      pk.groups = 8;
-      grid = cus - cus % 8;
-    } else {
-      pk.groups = 1;
-      grid = (int)(pairs < cus ? pairs : (cus > 0 ? cus : 1));
-    }
-    void* args[] = {&pk};
+    const int grid_k = grid_for(pk, (long long)pk.BH * ((pk.nblk + 1) / 2));
+    void* args_k[] = {&pk};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<D, CAUSAL, OUT_F32, GEN>),
-                        dim3(grid), dim3(kThreadsK), args, 0, stream);
+                        dim3(grid_k), dim3(kThreadsK), args_k, 0, stream);
     if (e != hipSuccess) return e;
-  }
-  {
+    // dQ: query blocks taken from the item queues
     p.nblk = (a.Tq + kOwnQ - 1) / kOwnQ;
-    void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(
-        reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, OUT_F32, GEN>),
-        dim3(p.BH * p.nblk), dim3(kThreadsQ), args, 0, stream);
+    const int grid_q = grid_for(p, (long long)p.BH * p.nblk);
+    void* args_q[] = {&p};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, OUT_F32, GEN>),
+                        dim3(grid_q), dim3(kThreadsQ), args_q, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

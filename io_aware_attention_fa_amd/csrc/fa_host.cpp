@@ -126,10 +126,12 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   fa::BwdLaunch a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  // the workspace holds two arrays of B*h*Tq floats, the second on a 256-byte boundary
-  const size_t half = fa_bwd_workspace_size(B, h, Tq) / 2;
+  // the workspace holds two arrays of B*h*Tq floats, each from a 256-byte boundary, then the
+  // item counters
+  const size_t arr = (static_cast<size_t>(B * h * Tq) * sizeof(float) + 255) / 256 * 256;
   a.l2 = static_cast<float*>(workspace);
-  a.dd = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
+  a.dd = reinterpret_cast<float*>(static_cast<char*>(workspace) + arr);
+  a.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 2 * arr);
   a.B = static_cast<int>(B); a.H = static_cast<int>(h);
   a.Tq = static_cast<int>(Tq); a.Tk = static_cast<int>(Tk); a.d = static_cast<int>(d);
   a.causal = causal != 0; a.out_f32 = out_f32; a.scale = scale;

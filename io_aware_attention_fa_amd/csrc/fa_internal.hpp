@@ -45,6 +45,7 @@ struct BwdLaunch {
   void* dv;
   float* l2;   // workspace: LSE * log2(e) per query row
   float* dd;   // workspace: D_i = <dO_i, O_i> per query row
+  uint32_t* ctr;   // workspace: 1 KB of item counters of the persistent kernels
   int B, H, Tq, Tk, d;
   bool causal;
   bool out_f32;

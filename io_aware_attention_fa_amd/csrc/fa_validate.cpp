@@ -185,12 +185,15 @@ extern "C" int fa_validate_decode_strided(const void* q, const void* k, const vo
 
 namespace {
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+// the backward's item counters: 2 kernels x 8 queues, 64 bytes apart (fa_bwd_kernel.hip)
+constexpr size_t kBwdCounterBytes = 1024;
 }  // namespace
 
 extern "C" size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq) {
   if (B < 1 || h < 1 || Tq < 1) return 0;
   return 2 * round256(static_cast<size_t>(B) * static_cast<size_t>(h) * static_cast<size_t>(Tq) *
-                      sizeof(float));
+                      sizeof(float)) +
+         kBwdCounterBytes;
 }
 
 extern "C" int fa_validate_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -131,9 +131,10 @@ def test_bwd_causal_t4096_d128_full_size(gpu):
 
 def test_bwd_persistent_schedule_more_pairs_than_cus(gpu):
     """111 heads (not a multiple of the 8 XCD groups) and 9 key blocks per head (an odd count:
-    a middle block without a partner): 555 key-block pairs for the persistent dK/dV grid.  Every
-    gradient element is written (outputs start as NaN), and sampled heads, among them the last
-    heads of several groups, match the oracle."""
+    a middle block without a partner): 555 key-block pairs for the persistent dK/dV grid, and
+    555 query blocks in dQ's eight item queues of unequal length (14 or 13 heads: workgroups
+    take from other queues at the end).  Every gradient element is written (outputs start as
+    NaN), and sampled heads, among them the last heads of several groups, match the oracle."""
     B, h, T, d = 3, 37, 1100, 128
     log(f"[case] bwd persistent B={B} h={h} T={T} d={d}")
     wl = si.custom_workload(B, h, T, T, d, True, name="bwd_persistent")
