@@ -317,9 +317,11 @@ __device__ __forceinline__ void take_item(const BwdParams& p, uint32_t* ctr, int
 
 // Runs body(bh, blk, tid, claim, publish) for every item this workgroup takes.  One lane (lane 0
 // of wave 0) takes items; the item is passed to the waves through a two-int LDS slot.  The body
-// calls claim() as its first loads are issued (the counter's atomic then completes with them:
-// its result is read only after the body has waited for all of its loads) and publish(c) after
-// its first barrier (every wave has read the slot by then).  tid is the thread index, rebuilt
+// calls claim() as its last step ends and publish(c) after its stores (the counter's atomic
+// completes during the stores; every wave read the slot at the item's start).  Taking the next
+// item only then keeps the items a queue's workgroups run at one time contiguous in the queue,
+// so they share their heads' tiles in L2: taken one item ahead (at an item's start), the short
+// blocks of a head ran long after its long ones and fetched 2.6 times the bytes.  tid is the thread index, rebuilt
 // per item as in for_each_block.  The barrier between items lets the next item's loads reuse
 // the LDS.
 template <bool REV, class F>
@@ -992,10 +994,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
       __syncthreads();
     };
     for (int it = 0; it < AHEAD - 1 && it < nt; ++it) request(it);
-    const int next = claim();
     wait_tile<PER, AHEAD - 2>(1, min(AHEAD - 2, nt - 1));
     __syncthreads();
-    publish(next);
     step(Parts<false, false, true, true>{}, Stage<NST - 1>{}, -1);
     step(Parts<false, true, true, true>{}, Stage<0>{}, 0);
     // steps 1 .. nt: a chain of the NST stage variants, left after step nt; each step in a masked
@@ -1020,6 +1020,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
       while (!fin) fin = chain(Parts<true, true, true, true>{});
     }
 
+    const int next = claim();   // the next item, taken as this one ends
     if constexpr (OUT_F32 || GEN) {   // (through LDS the strided variant spills in its steps)
       if (qrow < p.Tq) {
         const size_t row = (size_t)(head_elem<D, GEN>(p, p.ldq, bh, p.Tq) +
@@ -1044,6 +1045,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
       store_rows_bf16<D, GEN>(accq, p.scale, lk + (uint32_t)wave * (32u * (2 * D + 16)),
                               lane & 31, g, qw0, p.Tq, rd, rs, hd);
     }
+    publish(next);
   });
 }
 
