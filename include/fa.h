@@ -288,11 +288,13 @@ int fa_gelu_bf16(const void* x, void* y, int64_t n, void* stream);
  *   [rows][cols] bf16 activation with one bf16 bias per column (page "Fusion and IO-aware
  *   kernels", "The idea in one minute": bias add, GELU and dropout as one kernel that reads x once
  *   and writes y once).  Arithmetic in fp32, y rounded to bf16 (round to nearest even).
- *   Dropout: element e = row * cols + col draws word e % 4 of Philox4x32-10 (Salmon et al.,
- *   "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter (e / 4 low 32 bits,
- *   e / 4 high 32 bits, offset low, offset high) and key (seed low, seed high); it is dropped
- *   (y = 0) iff that word is below floor(p * 2^32), else y = gelu(x + bias) * (1 / (1 - p)) with
- *   the factor rounded to fp32.  The same (seed, offset) reproduces the same mask bit for bit.
+ *   Dropout: element e = row * cols + col draws 16 bits, half e % 2 (low 16 bits for even e,
+ *   high for odd) of word (e % 8) / 2 of Philox4x32-10 (Salmon et al., "Parallel random
+ *   numbers: as easy as 1, 2, 3", SC 2011) at counter (e / 8 low 32 bits, e / 8 high 32 bits,
+ *   offset low, offset high) and key (seed low, seed high); it is dropped (y = 0) iff that value
+ *   is below floor(p * 2^16), else y = gelu(x + bias) * (1 / (1 - p)) with the factor rounded to
+ *   fp32.  The drop probability is p to within 2^-16.  The same (seed, offset) reproduces the
+ *   same mask bit for bit.
  *   Preconditions: rows, cols >= 1; 0 <= p < 1 (else FA_ERR_PROB); x, bias, y 2-byte aligned
  *   (16-byte aligned with cols % 8 == 0 and rows <= 65535 takes the vector path); y equal to x
  *   or not overlapping it.

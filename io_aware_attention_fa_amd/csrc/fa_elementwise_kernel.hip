@@ -8,16 +8,18 @@
 // u = sqrt(2/pi) (x + 0.044715 x^3) (the same function: 0.5 (1 + tanh u) = 1 / (1 + e^(-2u))).
 //
 // Dropout draws from Philox4x32-10 (Salmon et al., SC 2011), written here from its published
-// definition: element e of the row-major activation uses word e % 4 of the generator applied to
-// the counter (e / 4 low, e / 4 high, offset low, offset high) under the key (seed low, seed
-// high), and is dropped iff that word is below floor(p * 2^32); kept elements are scaled by
-// 1 / (1 - p).  The decision is an integer comparison, so it is reproducible bit for bit.
+// definition: element e of the row-major activation uses 16 bits, half e % 2 (low for even e)
+// of word (e % 8) / 2 of the generator applied to the counter (e / 8 low, e / 8 high, offset
+// low, offset high) under the key (seed low, seed high), and is dropped iff that value is below
+// floor(p * 2^16); kept elements are scaled by 1 / (1 - p).  One generator call thus serves
+// eight elements (its 40 64-bit multiplies per call had made the kernel bound by them rather
+// than by HBM).  The decision is an integer comparison, so it is reproducible bit for bit.
 //
 // MI355X mapping (our design): streaming kernels with 16-byte nontemporal loads and stores,
 // 4 (fp32) or 8 (bf16) elements per lane per access, several accesses in flight per lane; the
-// dropout kernel gives each lane 8 consecutive columns of two rows (two Philox blocks per row)
-// so that the bias needs no division by the row length and is unpacked once for both rows.  Lengths that do not fit the vector layout take a
-// scalar path.
+// dropout kernel gives each lane 8 consecutive columns of two rows (one Philox block per row),
+// so that the bias needs no division by the row length and is unpacked once for both rows.
+// Lengths that do not fit the vector layout take a scalar path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -147,10 +149,13 @@ struct DropoutParams {
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
 };
 
-// Computed for every element and selected, so that the wave never branches on the mask.
-__device__ __forceinline__ float dropout_one(float xb, uint32_t word, const DropoutParams& p) {
+// Computed for every element and selected, so that the wave never branches on the mask.  The
+// element's 16-bit draw is compared in the high half of a word: bits is the generator word for
+// an odd element and the word shifted left by 16 for an even one, and p.threshold is
+// floor(p * 2^16) * 2^16.
+__device__ __forceinline__ float dropout_one(float xb, uint32_t bits, const DropoutParams& p) {
   const float g = gelu(xb) * p.scale;
-  return word >= p.threshold ? g : 0.f;
+  return bits >= p.threshold ? g : 0.f;
 }
 
 // Vector path (cols % 8 == 0, 16-byte aligned rows): lane -> the same 8 consecutive columns of
@@ -158,18 +163,14 @@ __device__ __forceinline__ float dropout_one(float xb, uint32_t word, const Drop
 // and both rows' loads are in flight together.
 __device__ __forceinline__ u32x4_t dropout_8(u32x4_t a, const float (&bf)[8], int64_t e,
                                             const DropoutParams& p) {
-  const uint64_t blk = (uint64_t)e >> 2;
-  const Philox4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.off_lo, p.off_hi,
-                                   p.seed_lo, p.seed_hi);
-  const Philox4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.off_lo,
-                                   p.off_hi, p.seed_lo, p.seed_hi);
+  const uint64_t blk = (uint64_t)e >> 3;   // e is a multiple of 8: one generator block
+  const Philox4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.off_lo, p.off_hi,
+                                  p.seed_lo, p.seed_hi);
   float r[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const Philox4& w = j < 2 ? w0 : w1;
-    const int k = (2 * j) & 3;
-    r[2 * j] = dropout_one(bf16_lo(a[j]) + bf[2 * j], w.v[k], p);
-    r[2 * j + 1] = dropout_one(bf16_hi(a[j]) + bf[2 * j + 1], w.v[k + 1], p);
+  for (int j = 0; j < 4; ++j) {   // elements 2j and 2j + 1: the two halves of word j
+    r[2 * j] = dropout_one(bf16_lo(a[j]) + bf[2 * j], w.v[j] << 16, p);
+    r[2 * j + 1] = dropout_one(bf16_hi(a[j]) + bf[2 * j + 1], w.v[j], p);
   }
   const u32x2_t lo = pack_bf16x4(r[0], r[1], r[2], r[3]);
   const u32x2_t hi = pack_bf16x4(r[4], r[5], r[6], r[7]);
@@ -204,11 +205,12 @@ __global__ __launch_bounds__(kThreadsEw) void fa_bias_gelu_dropout_scalar_kernel
   const int64_t stride = (int64_t)gridDim.x * kThreadsEw;
   for (int64_t e = (int64_t)blockIdx.x * kThreadsEw + threadIdx.x; e < n; e += stride) {
     const int64_t col = e % p.cols;
-    const uint64_t blk = (uint64_t)e >> 2;
+    const uint64_t blk = (uint64_t)e >> 3;
     const Philox4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.off_lo, p.off_hi,
                                     p.seed_lo, p.seed_hi);
+    const uint32_t word = w.v[(e >> 1) & 3];
     const float xb = bf16_lo(p.x[e]) + bf16_lo(p.bias[col]);
-    const u32x2_t o = pack_bf16x4(dropout_one(xb, w.v[e & 3], p), 0.f, 0.f, 0.f);
+    const u32x2_t o = pack_bf16x4(dropout_one(xb, (e & 1) ? word : word << 16, p), 0.f, 0.f, 0.f);
     p.y[e] = (uint16_t)o[0];
   }
 }

@@ -227,9 +227,10 @@ extern "C" int fa_bias_gelu_dropout_bf16(const void* x, const void* bias, void* 
   if (st != FA_OK) return st;
   fa::DropoutLaunch a;
   a.x = x; a.bias = bias; a.y = y; a.rows = rows; a.cols = cols;
-  // drop iff word < floor(p * 2^32); kept values scaled by 1 / (1 - p)
-  const double t = std::floor(static_cast<double>(p) * 4294967296.0);
-  a.threshold = t >= 4294967295.0 ? 0xffffffffu : static_cast<uint32_t>(t);
+  // drop iff the element's 16-bit draw < floor(p * 2^16) (compared in the high half of a word,
+  // so the threshold is scaled by 2^16); kept values scaled by 1 / (1 - p)
+  const double t = std::floor(static_cast<double>(p) * 65536.0);
+  a.threshold = static_cast<uint32_t>(t >= 65535.0 ? 65535.0 : t) << 16;
   a.scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
   a.seed = seed; a.offset = offset;
   return map_hip(fa::launch_bias_gelu_dropout(a, static_cast<hipStream_t>(stream)));

@@ -73,7 +73,7 @@ struct DropoutLaunch {
   const void* bias;
   void* y;
   int64_t rows, cols;
-  uint32_t threshold;   // drop iff the element's generator word is below it
+  uint32_t threshold;   // floor(p * 2^16) * 2^16: drop iff the element's draw * 2^16 is below it
   float scale;          // 1 / (1 - p)
   uint64_t seed, offset;
 };

@@ -12,11 +12,13 @@ What it computes:
     GPU kernel implement from that published definition.
 
 Readings where the pages are silent:
-  * element e of the row-major activation draws word e % 4 of Philox4x32-10 applied to the
-    counter (e // 4 low 32 bits, e // 4 high 32 bits, offset low, offset high) under the key
-    (seed low, seed high);
-  * it is dropped iff that word is below floor(p * 2^32) (an integer comparison, so both sides
-    take the same decision exactly), and kept elements are scaled by 1 / (1 - p); p in [0, 1).
+  * element e of the row-major activation draws a 16-bit value: half e % 2 (the low 16 bits for
+    even e, the high 16 bits for odd e) of word (e % 8) // 2 of Philox4x32-10 applied to the
+    counter (e // 8 low 32 bits, e // 8 high 32 bits, offset low, offset high) under the key
+    (seed low, seed high), so one generator call serves eight elements;
+  * it is dropped iff that value is below floor(p * 2^16) (an integer comparison, so both sides
+    take the same decision exactly; the drop probability is p to within 2^-16), and kept
+    elements are scaled by 1 / (1 - p); p in [0, 1).
 
 Every function here is pinned in ``tests/test_oracle_elementwise.py`` (the generator's published
 known-answer vectors, identities of the tanh form, scipy's logistic function, the p = 0 case and
@@ -69,22 +71,24 @@ def philox4x32_10(counter, key):
 
 
 def dropout_threshold(p: float) -> int:
-    """Words below this integer are dropped: floor(p * 2^32), for p in [0, 1)."""
+    """Draws below this integer are dropped: floor(p * 2^16), for p in [0, 1)."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(math.floor(p * 4294967296.0)), _MASK32)
+    return min(int(math.floor(p * 65536.0)), 0xFFFF)
 
 
 def dropout_words(n: int, seed: int, offset: int, first: int = 0):
-    """The generator word of elements first .. first + n - 1 (see the module docstring)."""
+    """The 16-bit draws of elements first .. first + n - 1 (see the module docstring)."""
     e = np.arange(first, first + n, dtype=np.uint64)
-    blk = e // np.uint64(4)
+    blk = e // np.uint64(8)
     ctr = np.stack([blk & np.uint64(_MASK32), blk >> np.uint64(32),
                     np.full_like(blk, offset & _MASK32), np.full_like(blk, (offset >> 32) & _MASK32)],
                    axis=1)
     key = np.tile(np.array([seed & _MASK32, (seed >> 32) & _MASK32], dtype=np.uint64), (n, 1))
     words = philox4x32_10(ctr, key)
-    return words[np.arange(n), (e % np.uint64(4)).astype(np.int64)]
+    word = words[np.arange(n), ((e % np.uint64(8)) // np.uint64(2)).astype(np.int64)]
+    shift = (e % np.uint64(2)) * np.uint64(16)
+    return ((word.astype(np.uint64) >> shift) & np.uint64(0xFFFF)).astype(np.uint32)
 
 
 def bias_gelu_dropout(x, bias, p: float, seed: int, offset: int, first_row: int = 0):

@@ -58,17 +58,19 @@ def test_gelu_identities():
 
 def test_dropout_threshold():
     assert eref.dropout_threshold(0.0) == 0
-    assert eref.dropout_threshold(0.5) == 2 ** 31
-    assert eref.dropout_threshold(0.1) == math.floor(0.1 * 2 ** 32)
+    assert eref.dropout_threshold(0.5) == 2 ** 15
+    assert eref.dropout_threshold(0.1) == math.floor(0.1 * 2 ** 16) == 6553
+    assert eref.dropout_threshold(0.99999) == 65535
     with pytest.raises(ValueError):
         eref.dropout_threshold(1.0)
 
 
 def test_dropout_words_follow_the_counter_layout():
-    w = eref.dropout_words(12, seed=0x1234_5678_9ABC_DEF0, offset=7)
-    for e in range(12):
-        blk = e // 4
-        ref = eref.philox4x32_10([[blk, 0, 7, 0]], [[0x9ABCDEF0, 0x12345678]])[0][e % 4]
+    w = eref.dropout_words(24, seed=0x1234_5678_9ABC_DEF0, offset=7)
+    for e in range(24):
+        blk = e // 8
+        word = int(eref.philox4x32_10([[blk, 0, 7, 0]], [[0x9ABCDEF0, 0x12345678]])[0][(e % 8) // 2])
+        ref = (word >> 16) if e % 2 else (word & 0xFFFF)
         assert w[e] == ref
     # a window starting mid-stream sees the same words
     assert np.array_equal(eref.dropout_words(5, 99, 3, first=6), eref.dropout_words(11, 99, 3)[6:])
@@ -90,8 +92,9 @@ def test_bias_gelu_dropout_rules():
 
 
 def test_keep_rate_matches_p():
+    words = eref.dropout_words(200_000, seed=2024, offset=1)
+    assert words.max() <= 0xFFFF
     for p in (0.1, 0.5, 0.9):
-        words = eref.dropout_words(200_000, seed=2024, offset=1)
         kept = np.mean(words >= np.uint32(eref.dropout_threshold(p)))
         sigma = math.sqrt(p * (1 - p) / words.size)
         assert abs(kept - (1 - p)) <= 5 * sigma

@@ -108,8 +108,13 @@ ELEMENTWISE_MUTANTS = {
     "dropout without the rescale": ("np.where(keep, g / (1.0 - p), 0.0)", "np.where(keep, g, 0.0)"),
     "dropout decision inverted": ("keep = words >= np.uint32(dropout_threshold(p))",
                                   "keep = words < np.uint32(dropout_threshold(p))"),
-    "words indexed by block": ("return words[np.arange(n), (e % np.uint64(4)).astype(np.int64)]",
-                               "return words[np.arange(n), 0]"),
+    "words indexed by block": (
+        "word = words[np.arange(n), ((e % np.uint64(8)) // np.uint64(2)).astype(np.int64)]",
+        "word = words[np.arange(n), 0]"),
+    "one half of each word": ("shift = (e % np.uint64(2)) * np.uint64(16)",
+                              "shift = np.zeros_like(e)"),
+    "32-bit threshold": ("return min(int(math.floor(p * 65536.0)), 0xFFFF)",
+                         "return min(int(math.floor(p * 4294967296.0)), 0xFFFFFFFF)"),
 }
 
 
