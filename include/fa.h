@@ -138,7 +138,8 @@ size_t fa_decode_workspace_size(int64_t B, int64_t h, int64_t d_head, int64_t nu
  *   of 8 in [8, 128], padded to 64 or 128 with zeros on chip).
  *   Preconditions: as fa_fwd for pointers and sizes; 1 <= num_splits <= min(Tk, FA_MAX_SPLITS);
  *   workspace 16-byte aligned with workspace_bytes >= fa_decode_workspace_size(B, h, d_head,
- *   num_splits).  The workspace holds no state between calls.
+ *   num_splits).  The workspace holds no state between calls; calls that may run at the same
+ *   time (on different streams) need separate workspaces.
  */
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t h, int64_t Tk, int64_t d_head, float scale,
@@ -209,7 +210,8 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t h, int64_t Tq);
  *   Preconditions: as fa_fwd for sizes and alignment (all tensors 16-byte aligned, lse 4-byte);
  *   workspace 16-byte aligned with workspace_bytes >= fa_bwd_workspace_size(B, h, Tq); the
  *   outputs and the workspace must not overlap the inputs or each other.  Every element of dq,
- *   dk and dv is written.  The workspace holds no state between calls.
+ *   dk and dv is written.  The workspace holds no state between calls; calls that may run at
+ *   the same time (on different streams) need separate workspaces.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
