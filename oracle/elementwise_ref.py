@@ -49,8 +49,8 @@ def philox4x32_10(counter, key):
     """Philox4x32 with 10 rounds on arrays of counters [n][4] and keys [n][2] (uint32 values).
 
     One round: (hi0, lo0) = M0 * c0 and (hi1, lo1) = M1 * c2 as 64-bit products; the new counter
-    is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); then the key is bumped by (W0, W1).  The key is
-    used unbumped in round 1 and bumped before each later round.
+    is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); then the key is bumped by (W0, W1).  The first
+    of the ten Philox rounds uses the key as given; each later one uses it bumped once more.
     """
     c = np.array(counter, dtype=np.uint64).reshape(-1, 4)
     k = np.array(key, dtype=np.uint64).reshape(-1, 2)
