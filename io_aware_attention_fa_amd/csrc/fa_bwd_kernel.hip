@@ -414,8 +414,9 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p, int64_t r
 // are loaded AHEAD steps ahead into a ring of NST stages; the stage of every step is a
 // compile-time constant (the steady state is a chain of the NST stage variants, left after the
 // last step), so that all LDS addresses are per-lane registers plus immediates.  The last steps
-// run every part: their V and A parts read stages holding stale tiles and produce values that
-// are never used.
+// run the V part (and, in the dK/dV kernel, the A part) on stages holding stale tiles and produce
+// values that are never used; the dQ kernel skips its A part there behind one wave-uniform
+// branch (the same branch in the dK/dV roles measured no faster, and in role V it spills).
 
 // A step's MFMA stream: NC C-part MFMAs, then NA A-part MFMAs, with RING operands in flight.
 // The stream is issued in program order (a scheduling barrier after each MFMA): left to itself
@@ -973,22 +974,36 @@ void fa_bwd_dq_kernel(BwdParams p) {
       // MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not depend on it
       // (the A part overwrites the scores it reads, so it comes last).
 #pragma unroll
-      for (int i = 0; i < S::n; ++i) {
+      for (int i = 0; i < nc; ++i) {
         const bf16x8_t a = ring[i % kRing];
         if (i + kRing < S::n)
           ring[i % kRing] = opnd(i + kRing);
         else if (next)
           ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
-        if (i < nc) {
-          accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
-        } else {
+        accq[i % ND] = mfma_32x32x16(a, dsb[PC][i / ND], accq[i % ND]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // The A part's tile s + 1 exists only for s + 1 < nt: the last two steps skip it (one
+      // wave-uniform branch) and only read the next step's first operands.
+      if (s + 1 < nt) {
+#pragma unroll
+        for (int i = nc; i < S::n; ++i) {
+          const bf16x8_t a = ring[i % kRing];
+          if (i + kRing < S::n)
+            ring[i % kRing] = opnd(i + kRing);
+          else if (next)
+            ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
           const int j = i - nc, ss = (j >> 1) / KB, kb = (j >> 1) % KB;
           if (j & 1)
             dpacc[kb] = mfma_32x32x16(a, dof[ss], ss == 0 ? f32x16_t{} : dpacc[kb]);
           else
             sacc[kb] = mfma_32x32x16(a, qf[ss], ss == 0 ? f32x16_t{} : sacc[kb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (next) {
+#pragma unroll
+        for (int i = (nc > S::n - kRing ? nc : S::n - kRing); i < S::n; ++i)
+          ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
       }
       wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
       __syncthreads();
