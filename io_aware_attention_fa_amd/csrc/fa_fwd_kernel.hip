@@ -120,13 +120,14 @@ constexpr int kVmcntQTile = vmcnt_imm(D / 16 + 2 * Tile<D>::LOADS_PER_WAVE);
 // Matrix sections (see the kernel): scores only (first tile of a block), both products, or the
 // P^T product only (after the last tile).
 constexpr int kSecScores = 0, kSecBoth = 1, kSecValues = 2;
-constexpr int kRing = 4;   // operand registers in flight per matrix section
 
 // Operand order of a matrix section: scores only = the NK K operands; both = VH V^T operands,
 // the NK K operands, the other NV - VH V^T operands; values only = the NV V^T operands.  kPre
-// operands are in the ring on entry.  K operands take one LDS read, V^T operands two.
-template <int MODE, int NV, int NK, int VH>
+// operands are in the ring of kRing registers on entry.  K operands take one LDS read, V^T
+// operands two.
+template <int MODE, int NV, int NK, int VH, int RING>
 struct OpSeq {
+  static constexpr int kRing = RING;
   static constexpr int n = MODE == kSecScores ? NK : (MODE == kSecBoth ? NV + NK : NV);
   static constexpr bool kScores = MODE != kSecValues;
   static constexpr int kPre = MODE == kSecScores ? kRing : (VH < kRing ? VH : kRing);
@@ -201,6 +202,10 @@ void fa_fwd_kernel(FwdParams p) {
   constexpr int ND = D / 32;   // 32-row blocks of O^T
   constexpr int NK = 2 * NS, NV = 4 * ND;            // K and V^T operands per tile
   constexpr int VH = NV / 2;                         // V^T operands before the scores
+  // Operand registers in flight per matrix section: 8 for the causal contiguous kernels (1-2%
+  // faster than 4 there), 4 elsewhere (the non-causal kernels ran 1% slower with 8, and the
+  // general-layout ones spill).
+  constexpr int kRing = CAUSAL && !GEN ? 8 : 4;
   constexpr int PRE = VH < kRing ? VH : kRing;       // of which read ahead of the barrier
   // LDS: the four K stages, then the four V stages.  Every access below is a per-lane base
   // address (fixed for the whole kernel) plus a compile-time offset below 64 KB, which the
@@ -357,7 +362,7 @@ void fa_fwd_kernel(FwdParams p) {
   bf16x8_t pb[4];
   // On entry ring[0 .. kPre-1] hold the first operands (kPre: kRing for scores only, else PRE).
   auto section = [&](auto mode, uint32_t ks, uint32_t vs) {
-    using S = OpSeq<decltype(mode)::value, NV, NK, VH>;
+    using S = OpSeq<decltype(mode)::value, NV, NK, VH, kRing>;
     constexpr int pre = S::kPre;
     auto opnd = [&](int i) {
       return S::is_k(i) ? k_opnd(ks, S::k_index(i)) : v_opnd(vs, S::v_index(i));
