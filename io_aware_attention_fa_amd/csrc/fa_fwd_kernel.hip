@@ -201,9 +201,10 @@ void fa_fwd_kernel(FwdParams p) {
   constexpr int NS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int ND = D / 32;   // 32-row blocks of O^T
   constexpr int NK = 2 * NS, NV = 4 * ND;            // K and V^T operands per tile
-  // V^T operands before the scores: half at d = 128; a quarter at d = 64, where the scores are
-  // half as long and the vector section that waits for them sets the pace (3-4% faster there)
-  constexpr int VH = D == 64 ? NV / 4 : NV / 2;
+  // V^T operands before the scores: half for the causal d = 128 kernels; a quarter elsewhere
+  // (3-4% faster at d = 64, where the scores are half as long and the vector section that waits
+  // for them sets the pace; 1% faster non-causal at d = 128; 2-3% slower causal at d = 128)
+  constexpr int VH = D == 128 && CAUSAL ? NV / 2 : NV / 4;
   // Operand registers in flight per matrix section: 8 for the causal contiguous kernels (1-2%
   // faster than 4 there), 4 elsewhere (the non-causal kernels ran 1% slower with 8, and the
   // general-layout ones spill).
