@@ -972,7 +972,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
       }
       // MFMAs in program order (pinned by scheduling barriers): operand i + kRing is read while
       // MFMA i runs, and the V part's chunks follow the C-part MFMAs, which do not depend on it
-      // (the A part overwrites the scores it reads, so it comes last).
+      // (the A part overwrites the scores it reads, so it comes last).  The MFMA parts run at
+      // raised issue priority, so that on a SIMD the wave past its V part keeps the matrix core
+      // fed while the other still issues its vector work (about 1% faster per backward call).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < nc; ++i) {
         const bf16x8_t a = ring[i % kRing];
@@ -1005,6 +1008,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int i = (nc > S::n - kRing ? nc : S::n - kRing); i < S::n; ++i)
           ring[i % kRing] = c_opnd(so_v, i + kRing - S::n);
       }
+      __builtin_amdgcn_s_setprio(0);
       wait_tile<PER, AHEAD - 2>(s + 2, min(s + AHEAD, nt - 1));
       __syncthreads();
     };
