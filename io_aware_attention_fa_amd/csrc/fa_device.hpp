@@ -30,6 +30,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
+// The same load marked non-temporal (cache policy bit 1: `nt` on gfx950), for data read once.
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
+}
 
 // D = A(32x16) * B(16x32) + C(32x32), bf16 inputs, fp32 accumulate.
 // Lane l holds A row (l % 32) and B column (l % 32), each with 8 consecutive k-slots chosen by
