@@ -30,7 +30,10 @@ namespace fa {
 namespace {
 
 constexpr int kThreadsEw = 256;
-constexpr int kUnrollEw = 4;   // vector accesses in flight per lane
+// vector accesses in flight per lane: 1, with one 256-lane workgroup per 256 vectors (up to 65536
+// workgroups), ran the 64M-element fp32 GELU 7.6% faster than 4 per lane with a quarter of the
+// workgroups (same box), and 2 per lane 3.8% faster
+constexpr int kUnrollEw = 1;
 
 // -2 sqrt(2/pi) log2(e) and the cubic coefficient: gelu(x) = x / (1 + 2^(K1 x (1 + A x^2)))
 constexpr float kGeluK1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
