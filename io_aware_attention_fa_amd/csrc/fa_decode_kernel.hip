@@ -8,12 +8,13 @@
 // section 3): every chunk's (max, denominator, output) is brought onto the common max by
 // exp(m_s - m*) and summed.
 //
-// Split pass: grid (num_splits, h, B), 256 threads.  A key row of d bf16 is read by d/8 lanes
-// with 16-byte loads, so one wave-wide load covers 64*16 = 1 KB of consecutive key rows; each
-// lane issues U K-loads and U V-loads before using any of them, so every wave keeps 2*U*1 KB of
-// HBM reads in flight.  The loads are marked non-temporal: the cache is read once, and keeping it
-// out of the caches' normal replacement made the split pass 7-9% faster.  Each lane keeps its own online-softmax state for the keys it sees; the
-// states are merged across lanes and waves at the end with the same rescale.
+// Split pass: grid (num_splits, h, B), 4 to 16 waves per workgroup (enough to cover a chunk in
+// one pass).  A key row of d bf16 is read by d/8 lanes with 16-byte loads, so one wave-wide load
+// covers 64*16 = 1 KB of consecutive key rows; each lane issues U K-loads and U V-loads before
+// using any of them, so every wave keeps 2*U*1 KB of HBM reads in flight.  The loads are marked
+// non-temporal: the cache is read once, and keeping it out of the caches' normal replacement made
+// the split pass 7-9% faster.  Each lane keeps its own online-softmax state for the keys it sees;
+// the states are merged across lanes and waves at the end with the same rescale.
 //
 // Combine pass: one 64-lane wave per (batch, head) reads the num_splits partials, rescales and
 // writes O (bf16) and LSE (fp32).
@@ -67,8 +68,10 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&o)[N], f
 }
 
 // GEN = false: contiguous tensors with d = D; GEN = true: the strides and d of DecodeParams.
-template <int D, bool GEN>
-__global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams p) {
+// WAVES waves per workgroup (4, 8 or 16; the launch picks the fewest that cover a chunk in one
+// pass where possible).
+template <int D, bool GEN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void fa_decode_split_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;     // lanes per key row
   constexpr int KPW = 64 / LPK;  // key rows per wave-wide load
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams 
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-  constexpr int STEP = kWaves * KPW * kUnroll;   // keys per workgroup iteration
+  constexpr int STEP = WAVES * KPW * kUnroll;   // keys per workgroup iteration
   for (int base = k_begin + wave * KPW * kUnroll; base < k_end; base += STEP) {
     u32x4_t kr[kUnroll], vr[kUnroll];
 #pragma unroll
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams 
   }
 
   // merge the waves through LDS
-  __shared__ float sm_o[kWaves][D];
-  __shared__ float sm_ml[kWaves][2];
+  __shared__ float sm_o[WAVES][D];
+  __shared__ float sm_ml[WAVES][2];
   if (slot == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm_o[wave][8 * c + e] = o[e];
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecodeParams 
 #pragma unroll
     for (int e = 0; e < 8; ++e) ow[e] = sm_o[0][8 * tid + e];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 1; w < WAVES; ++w) {
       float o2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o2[e] = sm_o[w][8 * tid + e];
@@ -255,10 +258,20 @@ hipError_t launch(const DecodeLaunch& a, hipStream_t stream) {
   p.k_b = a.k_s[0]; p.k_h = a.k_s[1]; p.k_t = (uint32_t)a.k_s[2];
   p.v_b = a.v_s[0]; p.v_h = a.v_s[1]; p.v_t = (uint32_t)a.v_s[2];
   {
+    // Workgroup size: enough waves to cover a chunk in one pass (each wave takes kUnroll loads
+    // of 512 / D keys per pass), at least 4 and at most 16.  With the whole chunk's loads in
+    // flight at once the split pass ran 5.5% faster at 512-key chunks and d = 128 (16 waves
+    // against 4), and 1% faster at d = 64 (8 waves); 16 waves at d = 64, half of them idle,
+    // ran 9% slower.
+    constexpr int kKeysPerWave = (512 / D) * kUnroll;
+    const int need = (p.chunk + kKeysPerWave - 1) / kKeysPerWave;
+    const void* fn = need > 8   ? reinterpret_cast<const void*>(&fa_decode_split_kernel<D, GEN, 16>)
+                     : need > 4 ? reinterpret_cast<const void*>(&fa_decode_split_kernel<D, GEN, 8>)
+                                : reinterpret_cast<const void*>(&fa_decode_split_kernel<D, GEN, 4>);
+    const int waves = need > 8 ? 16 : need > 4 ? 8 : 4;
     void* args[] = {&p};
     const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_split_kernel<D, GEN>),
-                        dim3(a.num_splits, a.H, a.B), dim3(kThreads), args, 0, stream);
+        hipLaunchKernel(fn, dim3(a.num_splits, a.H, a.B), dim3(64 * waves), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   int BH = a.B * a.H;
