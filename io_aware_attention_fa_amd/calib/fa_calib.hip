@@ -4,7 +4,8 @@
 //   lds    : ds_read_b128 and ds_read_b64_tr_b16 bandwidth (conflict-free addresses)
 //   ldsmfma: MFMAs whose A operands stream from LDS (random bf16 data), with or without
 //            operand reuse and a share of fma/exp vector work, at two waves per SIMD
-//   hbm    : streaming read of a large buffer with 16-byte buffer loads
+//   hbm    : streaming read of a large buffer with 16-byte loads (grid-stride, and in
+//            contiguous 128 KB blocks per 16-wave workgroup)
 //   atomic : fp32 atomic adds (no return value) into an L2-sized or an HBM-sized buffer
 //   clock  : shader clock from s_memtime against the 100 MHz s_memrealtime counter
 // Every kernel reads and writes only inside the buffers it is given.
@@ -281,6 +282,25 @@ __global__ __launch_bounds__(256) void k_hbm_read(const u32x4_t* __restrict__ sr
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Streaming read in contiguous blocks (the access pattern of the decode's split pass): workgroup
+// g of 16 waves reads the 128 KB block g, each wave 8 KB as 8 consecutive 1 KB wave-wide loads,
+// all issued before any is used.  The result feeds a store that never happens (the data are
+// ones), so the loads cannot be dropped.
+__global__ __launch_bounds__(1024) void k_hbm_read_blocked(const u32x4_t* __restrict__ src,
+                                                           long n16, uint32_t* out) {
+  const long base = (long)blockIdx.x * 8192 + (long)(threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
+  u32x4_t a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const long i = base + 64 * u;
+    a[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc ^= a[u][u & 3];
+  if (acc == 0x12345678u) out[0] = acc;
+}
+
 // fp32 atomic adds without a return value (global_atomic_add_f32): each wave adds to one
 // 256-byte run of 64 floats per iteration; consecutive iterations of a wave move by a large odd
 // stride, so the runs spread over the buffer.  n_mask = (floats in the buffer) - 1, a power of
@@ -361,6 +381,12 @@ int calib_lds_mfma(float* out, int blocks, int iters, int reuse, int nv, void* s
 }
 int calib_hbm_read(const void* src, long n16, uint32_t* out, int blocks, void* s) {
   hipLaunchKernelGGL(k_hbm_read, dim3(blocks), dim3(256), 0, (hipStream_t)s,
+                     (const u32x4_t*)src, n16, out);
+  return (int)hipGetLastError();
+}
+int calib_hbm_read_blocked(const void* src, long n16, uint32_t* out, void* s) {
+  const long blocks = (n16 + 8191) / 8192;
+  hipLaunchKernelGGL(k_hbm_read_blocked, dim3((unsigned)blocks), dim3(1024), 0, (hipStream_t)s,
                      (const u32x4_t*)src, n16, out);
   return (int)hipGetLastError();
 }

@@ -111,6 +111,10 @@ def main():
         t = _time(lambda: lib.calib_hbm_read(ctypes.c_void_p(src.data_ptr()), n // 16,
                                              ctypes.c_void_p(outu.data_ptr()), blocks_h, st))
         res[f"hbm_read_GBps_blocks{blocks_h}"] = n / t / 1e9
+    t = _time(lambda: lib.calib_hbm_read_blocked(ctypes.c_void_p(src.data_ptr()),
+                                                 ctypes.c_long(n // 16),
+                                                 ctypes.c_void_p(outu.data_ptr()), st))
+    res["hbm_read_GBps_blocked_128KB_per_16_waves"] = n / t / 1e9
     dst = torch.empty_like(src)
     t = _time(lambda: dst.copy_(src))
     res["torch_copy_GBps_read_plus_write"] = 2 * n / t / 1e9
