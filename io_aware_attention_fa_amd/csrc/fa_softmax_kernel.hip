@@ -8,8 +8,9 @@
 // a partial sum by exp(m_part - m_new) when the max grows.
 //
 // MI355X mapping (our design, not the pages'):
-//   * One wave per row, four rows per workgroup, no LDS and no barriers.  Up to 8192 columns the
-//     whole row stays in registers: lane l holds, for chunk c, the 16-byte group of columns
+//   * Four waves per workgroup, no LDS and no barriers.  Up to 8192 columns a wave holds a
+//     whole row in registers (up to 4096 columns two rows each, the next row's loads issued
+//     before the current row is written): lane l holds, for chunk c, the 16-byte group of columns
 //     c*256 + 4*l .. +3 (fully coalesced 1 KB wave loads), read once with nontemporal hints.
 //   * Each lane reduces its own entries to (m, l) -- the max, then the sum of exp(x - m) with the
 //     exponentials kept in registers -- and the 64 lanes merge their pairs by the recurrence's
@@ -81,20 +82,15 @@ __device__ __forceinline__ void store_vec(float* __restrict__ r, int col, int co
   }
 }
 
-// Row held in registers: CH chunks of 64 * VEC columns.
+// Row held in registers: CH chunks of 64 * VEC columns.  Up to 16 chunks each wave takes rows
+// row0, row0 + W, ... (W waves in the grid, launched for two rows per wave), issuing the next
+// row's loads before it works on and stores the current one, so that reads and writes overlap:
+// 4-7% faster than one row per wave at 4096 and 2048 columns (bit-identical).  32 chunks hold
+// one row at a time (two would spill).
 template <int VEC, int CH>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void fa_softmax_reg_kernel(
-    const float* __restrict__ x, float* __restrict__ y, float* __restrict__ lse, int64_t rows,
-    int cols) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;   // whole waves leave; there is no barrier
-  const float* xr = x + row * cols;
-  float* yr = y + row * cols;
-  float v[CH * VEC];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) load_vec<VEC>(xr, (c * 64 + lane) * VEC, cols, v + c * VEC);
-  // this lane's (m, l): max, then the sum of exp(x - m), keeping the exponentials
+__device__ __forceinline__ void softmax_row(float* v, float* __restrict__ yr,
+                                            float* __restrict__ lse, int64_t row, int cols,
+                                            int lane) {
   float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int i = 0; i < CH * VEC; ++i) mx[i & 3] = fmaxf(mx[i & 3], v[i]);
@@ -106,7 +102,6 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fa_softmax_reg_kernel(
     ls[i & 3] += v[i];
   }
   const float l = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  // merge the 64 pairs: M = max m, L = sum l * exp(m - M)
   const float M = wave_max(m);
   const float f = exp_diff(m, M);
   const float L = wave_sum(l * f);
@@ -116,6 +111,44 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fa_softmax_reg_kernel(
 #pragma unroll
   for (int c = 0; c < CH; ++c) store_vec<VEC>(yr, (c * 64 + lane) * VEC, cols, v + c * VEC);
   if (lse != nullptr && lane == 0) lse[row] = M + fast_log2(L) * kLn2;
+}
+
+template <int VEC, int CH>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void fa_softmax_reg_kernel(
+    const float* __restrict__ x, float* __restrict__ y, float* __restrict__ lse, int64_t rows,
+    int cols) {
+  const int lane = threadIdx.x & 63;
+  const int64_t W = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;   // whole waves leave; there is no barrier
+  float va[CH * VEC];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    load_vec<VEC>(x + row * cols, (c * 64 + lane) * VEC, cols, va + c * VEC);
+  if constexpr (CH > 16) {
+    softmax_row<VEC, CH>(va, y + row * cols, lse, row, cols, lane);
+    return;
+  }
+  float vb[CH * VEC];
+  for (;;) {
+    const int64_t nb = row + W;
+    if (nb < rows) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        load_vec<VEC>(x + nb * cols, (c * 64 + lane) * VEC, cols, vb + c * VEC);
+    }
+    softmax_row<VEC, CH>(va, y + row * cols, lse, row, cols, lane);
+    if (nb >= rows) break;
+    const int64_t na = nb + W;
+    if (na < rows) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        load_vec<VEC>(x + na * cols, (c * 64 + lane) * VEC, cols, va + c * VEC);
+    }
+    softmax_row<VEC, CH>(vb, y + nb * cols, lse, nb, cols, lane);
+    if (na >= rows) break;
+    row = na;
+  }
 }
 
 // Streamed form for wide rows: (m, l) over tiles of kStreamChunks chunks, then a second pass.
@@ -167,16 +200,18 @@ hipError_t launch_vec(const SoftmaxLaunch& a, hipStream_t s) {
   const int64_t grid = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int chunks = (int)((a.cols + 64 * VEC - 1) / (64 * VEC));
   const dim3 g((unsigned)grid), b(64 * kRowsPerBlock);
+  // two rows a wave for the pipelined register kernel
+  const dim3 g2((unsigned)((a.rows + 2 * kRowsPerBlock - 1) / (2 * kRowsPerBlock)));
   const float* x = a.x;
   float* y = a.y;
   float* lse = a.lse;
   const int64_t rows = a.rows;
   const int cols = (int)a.cols;
-  if (chunks <= 1) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 1>), g, b, 0, s, x, y, lse, rows, cols);
-  else if (chunks <= 2) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 2>), g, b, 0, s, x, y, lse, rows, cols);
-  else if (chunks <= 4) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 4>), g, b, 0, s, x, y, lse, rows, cols);
-  else if (chunks <= 8) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 8>), g, b, 0, s, x, y, lse, rows, cols);
-  else if (chunks <= 16) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 16>), g, b, 0, s, x, y, lse, rows, cols);
+  if (chunks <= 1) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 1>), g2, b, 0, s, x, y, lse, rows, cols);
+  else if (chunks <= 2) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 2>), g2, b, 0, s, x, y, lse, rows, cols);
+  else if (chunks <= 4) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 4>), g2, b, 0, s, x, y, lse, rows, cols);
+  else if (chunks <= 8) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 8>), g2, b, 0, s, x, y, lse, rows, cols);
+  else if (chunks <= 16) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 16>), g2, b, 0, s, x, y, lse, rows, cols);
   else if (chunks <= 32) hipLaunchKernelGGL((fa_softmax_reg_kernel<VEC, 32>), g, b, 0, s, x, y, lse, rows, cols);
   else hipLaunchKernelGGL((fa_softmax_stream_kernel<VEC>), g, b, 0, s, x, y, lse, rows, cols);
   return hipGetLastError();
