@@ -43,6 +43,9 @@ def test_decode_b64_h32_tk8192_full_size(gpu):
 @pytest.mark.parametrize("B,h,Tk,d,S", [
     (1, 1, 1, 128, 1), (2, 3, 7, 64, 3), (2, 2, 5, 128, 4), (1, 4, 1000, 128, 16),
     (3, 2, 4097, 64, 7), (1, 1, 513, 128, 256), (2, 2, 300, 128, 256), (2, 2, 40, 128, 40), (1, 2, 100, 64, 1),
+    # chunks that take the 8-wave split workgroup (d = 128: 129-256 keys, d = 64: 257-512),
+    # the last chunk ragged
+    (2, 3, 1599, 128, 8), (2, 2, 3199, 64, 8),
 ])
 def test_decode_edge_shapes(gpu, B, h, Tk, d, S):
     wl = si.custom_workload(B, h, 1, Tk, d, False, decode=True, num_splits=S)
